@@ -1,0 +1,180 @@
+"""Fp64 CPU oracle for the attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it, and
+it shares no code with the HIP path: it neither imports ``softmax_free_score_amd``
+nor reads its headers or constants.
+
+Two independent fp64 implementations of the same closed form live here:
+
+* ``attn_fwd_c`` -- plain C loops (``attn_oracle.c``), OpenMP over query rows;
+  also the CPU baseline that the benchmark times.
+* ``attn_fwd_np`` -- a numpy transcription (library matmuls as the two
+  contraction steps, everything else elementwise in the pages' order).
+
+What each computes, with the pages it follows:
+
+* Yat ("Softmax-Free Attention in JAX/Flax NNX", "One module, two
+  compatibility functions"; "The Kernel Between the Roles", "What the
+  exponential was hired to do"): dots = q.k, d2 = |q|^2 + |k|^2 - 2 dots,
+  b = softplus(b_raw), eps = softplus(eps_raw) per head,
+  kappa = (dots + b)^2 / (max(d2, 0) + eps), kappa = 0 where masked,
+  mass = sum_j kappa, w = kappa / (mass + 1e-9), out = w @ v.
+* softmax ("NNX Scaled Dot-Product Attention", "Shapes and the three steps",
+  "Mask before softmax"): s = q.k / sqrt(d_k), blocked scores -inf, softmax
+  over keys after subtracting the row maximum, out = w @ v.
+* s^tau ("s^tau" forum post, core formula): s = q.k / sqrt(d_k),
+  phi = softplus(s) + 1e-6, tau = softplus(log_tau) + 1 per head,
+  w = phi^tau / sum phi^tau over allowed keys, out = w @ v.
+
+Readings of points the pages leave open (GQA mapping h -> h // (Hq/Hkv),
+causal j <= i with Tq == Tk, masked keys weigh exactly 0 in all branches,
+mass and max_score per branch) are those stated in ``attn_oracle.c``.
+
+Parity status: every function here is pinned by tests in
+``tests/test_oracle_pins.py`` (worked examples printed on the pages, closed
+forms, invariants and brute force).  The mass and max_score conventions for
+softmax and s^tau and the GQA mapping are conventions of this build, pinned
+only by brute force and self-consistency (parity unpinned by the pages).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+SOFTMAX, YAT, STAU = 0, 1, 2
+VARIANTS = {"softmax": SOFTMAX, "yat": YAT, "stau": STAU}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, IEEE arithmetic, OpenMP)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-shared", "-fPIC",
+           _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        d = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.oracle_attn_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64,
+                                        i64, i64, d, d, d, d, d, d,
+                                        ctypes.POINTER(i64), i64, d, d, d]
+        lib.oracle_attn_fwd.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _dptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _as_f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def attn_fwd_c(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False,
+               rows=None):
+    """C oracle.  q [B,Hq,Tq,dk], k [B,Hkv,Tk,dk], v [B,Hkv,Tk,dv] (any float
+    dtype; upcast exactly to fp64).  ``rows`` optionally lists flat row ids
+    (b*Hq + h)*Tq + i to evaluate.  Returns (out, mass, max_score); with
+    ``rows`` they are [n_rows, dv], [n_rows], [n_rows], otherwise shaped
+    [B,Hq,Tq,dv] and [B,Hq,Tq]."""
+    variant = VARIANTS.get(variant, variant)
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, Hq, Tq, dk = q.shape
+    _, Hkv, Tk, dv = v.shape
+    params = [_as_f64(p) for p in (b_raw, eps_raw, log_tau)]
+    if rows is None:
+        n = B * Hq * Tq
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows_arr.size
+    out = np.empty((n, dv), np.float64)
+    mass = np.empty(n, np.float64)
+    mx = np.empty(n, np.float64)
+    rc = _load().oracle_attn_fwd(
+        int(variant), int(bool(causal)), B, Hq, Hkv, Tq, Tk, dk, dv, _dptr(q), _dptr(k),
+        _dptr(v), *[_dptr(p) for p in params],
+        None if rows_arr is None else rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        n, _dptr(out), _dptr(mass), _dptr(mx))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_fwd rejected its arguments (code {rc})")
+    if rows is None:
+        return out.reshape(B, Hq, Tq, dv), mass.reshape(B, Hq, Tq), mx.reshape(B, Hq, Tq)
+    return out, mass, mx
+
+
+def softplus(x):
+    """log(1 + e^x) without overflow in either tail; softplus(0) = ln 2."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def attn_fwd_np(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False):
+    """numpy fp64 oracle; same contract as ``attn_fwd_c`` without ``rows``."""
+    variant = VARIANTS.get(variant, variant)
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, Hq, Tq, dk = q.shape
+    _, Hkv, Tk, dv = v.shape
+    if Hq % Hkv or (causal and Tq != Tk):
+        raise ValueError("bad shape")
+    g = Hq // Hkv
+    # query head h reads key/value head h // g
+    kh = np.repeat(k, g, axis=1)
+    vh = np.repeat(v, g, axis=1)
+    dots = q @ np.swapaxes(kh, -1, -2)  # (B,Hq,Tq,Tk)
+    allowed = np.ones((Tq, Tk), bool)
+    if causal:
+        allowed = np.tril(allowed)
+    if variant == YAT:
+        bias = softplus(b_raw)[None, :, None, None]
+        eps = softplus(eps_raw)[None, :, None, None]
+        d2 = (np.sum(q * q, -1, keepdims=True) + np.swapaxes(np.sum(kh * kh, -1, keepdims=True), -1, -2)
+              - 2.0 * dots)
+        kappa = (dots + bias) ** 2 / (np.maximum(d2, 0.0) + eps)
+        kappa = np.where(allowed, kappa, 0.0)
+        mass = kappa.sum(-1)
+        w = kappa / (mass[..., None] + 1e-9)
+        max_score = np.where(allowed, kappa, -np.inf).max(-1)
+    elif variant == SOFTMAX:
+        s = np.where(allowed, dots / np.sqrt(dk), -np.inf)
+        m = s.max(-1, keepdims=True)
+        e = np.exp(s - m)
+        mass = e.sum(-1)
+        w = e / mass[..., None]
+        max_score = m[..., 0]
+    elif variant == STAU:
+        s = dots / np.sqrt(dk)
+        tau = (softplus(log_tau) + 1.0)[None, :, None, None]
+        u = np.where(allowed, (softplus(s) + 1e-6) ** tau, 0.0)
+        mass = u.sum(-1)
+        w = u / mass[..., None]
+        max_score = np.where(allowed, s, -np.inf).max(-1)
+    else:
+        raise ValueError(f"unknown variant {variant}")
+    return w @ vh, mass, max_score
