@@ -1,0 +1,180 @@
+"""Benchmark: fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_yat]
+                    [--no-cpu-baseline]
+
+A step is one Yat forward (|k|^2 pre-pass + fused kernel, i.e. every step of
+the hot path) over the resident synthetic batch B=4, H=16, T=4096, d=128,
+bf16, causal.  The softmax branch of the same kernel skeleton is timed on the
+same inputs for the side-by-side figure.  Prints one JSON line.
+
+Algorithmic work per allowed (query, key) pair: 2*d_k + 2*d_v MFMA flops
+(elementwise maps and reductions not counted); causal pairs per head
+T(T+1)/2.  Durations are HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s and % bf16 MFMA peak (Yat vs softmax), B4 h16 T4096 d128"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def alg_flops(wl) -> float:
+    return float(wl.allowed_pairs) * 2.0 * (wl.dk + wl.dv)
+
+
+def alg_bytes(wl) -> float:
+    e = 2 if wl.dtype == "bf16" else 4
+    q = wl.B * wl.Hq * wl.Tq * wl.dk * e
+    kv = wl.B * wl.Hkv * wl.Tk * (wl.dk + wl.dv) * e
+    o = wl.B * wl.Hq * wl.Tq * wl.dv * e
+    stats = 2 * wl.B * wl.Hq * wl.Tq * 4
+    return float(q + kv + o + stats)
+
+
+def time_calls(fn, stream, steps, warmup):
+    """Average per-call duration (ms) by HIP events on `stream`, plus the
+    wall time of the whole timed region."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(per)), float(np.median(per)), wall
+
+
+def cpu_baseline(inp, variant, target_s=15.0):
+    """The fp64 C oracle on a strided sample of the query rows, timed on the
+    host cores; scaled to TFLOP/s with the same algorithmic count."""
+    import oracle
+    wl = inp.wl
+    q, k, v = inp.f64()
+    prm = {n: a.astype(np.float64) for n, a in inp.params().items()}
+    n_rows = wl.B * wl.Hq * wl.Tq
+
+    def pairs_of(rows):
+        i = rows % wl.Tq
+        return float(np.sum(i + 1)) if wl.causal else float(len(rows) * wl.Tk)
+
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    probe = np.arange(0, n_rows, max(1, n_rows // 256), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd_c(q, k, v, variant, causal=wl.causal, rows=probe, **prm)
+    t_probe = max(time.perf_counter() - t0, 1e-3)
+    stride = max(1, int(np.ceil(n_rows * t_probe / len(probe) / target_s)))
+    rows = np.arange(stride // 2, n_rows, stride, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd_c(q, k, v, variant, causal=wl.causal, rows=rows, **prm)
+    dt = time.perf_counter() - t0
+    flops = pairs_of(rows) * 2.0 * (wl.dk + wl.dv)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{variant}, every {stride}th query row of {wl.name} ({len(rows)} rows, "
+                      f"{pairs_of(rows):.3e} allowed pairs) in {dt:.1f} s, fp64 C loops, OpenMP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_yat")
+    ap.add_argument("--variant", default="yat")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention "
+              "forward shards over (batch, kv-head) with no exchange step; only the one-GPU "
+              "kernel is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from softmax_free_score_amd import attn
+    from softmax_free_score_amd.workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    if wl.dtype == "bf16":
+        t = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = t(inp.q_bits), t(inp.k_bits), t(inp.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v))
+    prm = {n: torch.from_numpy(a).to(dev) for n, a in inp.params().items()}
+    out = torch.empty((wl.B, wl.Hq, wl.Tq, wl.dv), dtype=q.dtype, device=dev)
+    mass = torch.empty((wl.B, wl.Hq, wl.Tq), dtype=torch.float32, device=dev)
+    mx = torch.empty_like(mass)
+    stream = torch.cuda.current_stream(dev)
+    ws = {}
+    for var in ("yat", "softmax", "stau"):
+        n = attn.workspace_bytes(q, k, v, var)
+        ws[var] = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+
+    def call(var):
+        return lambda: attn.attn_fwd(q, k, v, var, causal=wl.causal, out=out, mass=mass,
+                                     max_score=mx, workspace=ws[var], stream=stream.cuda_stream,
+                                     **prm)
+
+    flops = alg_flops(wl)
+    primary = args.variant
+    torch.cuda.synchronize()
+    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup)
+    others = {}
+    for var in wl.variants:
+        if var != primary:
+            m2, md2, _ = time_calls(call(var), stream, args.steps, args.warmup)
+            others[var] = {"ms": m2, "tflops": flops / (m2 * 1e-3) / 1e12,
+                           "frac_bf16_peak": flops / (m2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    value = flops / (mean_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} Tq{wl.Tq} Tk{wl.Tk} "
+                               f"dk{wl.dk} dv{wl.dv} {wl.dtype} "
+                               f"{'causal' if wl.causal else 'non-causal'}",
+                   "variant": primary, "global_batch": wl.B, "seq_len": wl.Tq,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": f"|k|^2 pre-pass + attn_fwd_bf16 ({primary}); flops = "
+                               f"{flops:.4e} per launch ({wl.allowed_pairs} allowed pairs x "
+                               f"2(dk+dv))",
+                     "median_ms": round(med_ms, 4)},
+        "alg_bytes_gbs": round(alg_bytes(wl) / (mean_ms * 1e-3) / 1e9, 1),
+        "wall_s_timed_region": round(wall, 3),
+    }
+    for var, r in others.items():
+        line[var] = {k2: round(v2, 4) for k2, v2 in r.items()}
+    if "softmax" in others:
+        # > 1 means the primary branch is faster than softmax on the same inputs
+        line[f"{primary}_speed_vs_softmax"] = round(others["softmax"]["ms"] / mean_ms, 4)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, primary)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * sfs_attn.h -- C ABI of the fused attention forward for MI355X (gfx950).
+ *
+ * One call evaluates, for every batch b, query head h and query row i,
+ *
+ *     w_ij = normalize_j( score(q_i, k_j) ),   out_i = sum_j w_ij v_j,
+ *
+ * with one of three score-to-weight maps:
+ *
+ *   ATTN_YAT      "Softmax-Free Attention in JAX/Flax NNX", section "One module,
+ *                 two compatibility functions" (the kernel branch):
+ *                 dots = q.k;  d2 = |q|^2 + |k|^2 - 2 dots;
+ *                 b = softplus(b_raw[h]), eps = softplus(eps_raw[h]);
+ *                 kappa = (dots + b)^2 / (max(d2, 0) + eps); masked kappa = 0;
+ *                 mass = sum_j kappa;  w = kappa / (mass + 1e-9).
+ *                 No 1/sqrt(d_k) scale.
+ *   ATTN_SOFTMAX  "NNX Scaled Dot-Product Attention", the displayed equation
+ *                 A = softmax(Q K^T / sqrt(d_k) + M), O = A V, with M = -inf on
+ *                 blocked keys ("Mask before softmax").
+ *   ATTN_STAU     "s^tau" forum post, core formula:
+ *                 s = q.k / sqrt(d_k); phi = softplus(s) + 1e-6;
+ *                 tau = softplus(log_tau[h]) + 1; w = phi^tau / sum_j phi^tau.
+ *
+ * Shapes follow "NNX Scaled Dot-Product Attention", "Shapes and the three
+ * steps": queries T_q x d_k, keys T_k x d_k, values T_k x d_v per head; T_q
+ * may differ from T_k and d_v from d_k.  Several query heads may share one
+ * key/value head (grouped-query attention): query head h reads key/value head
+ * h / (Hq / Hkv).
+ *
+ * Readings of points the pages leave open:
+ *   - causal: key j is allowed for query i iff j <= i; it requires T_q == T_k.
+ *   - a masked key contributes exactly 0 to numerator and denominator in all
+ *     three maps (the s^tau page instead feeds -inf through softplus).
+ *   - mass [B,Hq,Tq]: Yat sum(kappa); softmax sum_j exp(s_ij - max_j s_ij);
+ *     s^tau sum_j phi^tau.  A row whose s^tau mass underflows to 0 gets out 0.
+ *   - max_score [B,Hq,Tq]: Yat max kappa; softmax and s^tau max s (the scaled
+ *     logit), over allowed keys.
+ *   - s^tau is evaluated in one pass without a running maximum; its supported
+ *     domain is tau * ln(phi) < 88 (no fp32 overflow of phi^tau).
+ */
+#ifndef SFS_ATTN_H
+#define SFS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Score-to-weight map. */
+typedef enum { ATTN_SOFTMAX = 0, ATTN_YAT = 1, ATTN_STAU = 2 } attn_variant;
+
+/* Storage type of q, k, v and out.  Arithmetic is fp32 in both cases; with
+ * ATTN_BF16 the two contractions run on bf16 matrix cores with fp32
+ * accumulation and the weights are rounded to bf16 (nearest-even) before the
+ * second one. */
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Status codes: 0 on success, negative on error. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,       /* a size is negative or zero where it may not be,
+                                Hq % Hkv != 0, or causal with T_q != T_k */
+  ATTN_ERR_UNSUPPORTED = -3, /* dtype, variant or head size not built; a base
+                                pointer or stride breaks the 16-byte alignment
+                                rule; a per-head offset exceeds 2^31 elements */
+  ATTN_ERR_PARAM = -4,       /* a per-head parameter the variant needs is NULL */
+  ATTN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
+  ATTN_ERR_HIP = -6          /* the HIP runtime failed (no device, launch
+                                error); see attn_last_error() */
+};
+
+/* Problem description.  Sizes: B >= 0 batches, Hq >= 1 query heads,
+ * Hkv >= 1 key/value heads with Hq % Hkv == 0, T_q >= 0 query rows,
+ * T_k >= 1 key rows, d_k and d_v in {16, 32, 64, 128}.
+ *
+ * Strides are in elements for the (batch, head, row) axes of q [B,Hq,Tq,dk],
+ * k [B,Hkv,Tk,dk], v [B,Hkv,Tk,dv] and out [B,Hq,Tq,dv]; the last axis is
+ * contiguous.  Every stride must be a non-negative multiple of 16 bytes
+ * (8 bf16 or 4 fp32 elements). */
+typedef struct {
+  int64_t B, Hq, Hkv, Tq, Tk, dk, dv;
+  int32_t dtype; /* attn_dtype */
+  int32_t reserved;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} attn_desc;
+
+/* Fill *desc for densely packed [B,H,T,d] tensors.  Returns ATTN_OK or
+ * ATTN_ERR_NULL. */
+int attn_desc_init(attn_desc* desc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq,
+                   int64_t Tk, int64_t dk, int64_t dv, int32_t dtype);
+
+/* Device workspace, in bytes, that attn_fwd needs for this problem and map
+ * (ATTN_YAT keeps fp32 |k|^2 per key row there; the others need none).
+ * Returns 0 when none is needed or the description is invalid. */
+size_t attn_fwd_workspace_bytes(const attn_desc* desc, int variant);
+
+/* Attention forward.
+ *
+ * q, k, v, out   device memory in desc->dtype with the strides of desc; out
+ *                must not alias any input.
+ * variant        attn_variant.
+ * b_raw, eps_raw device fp32 [Hq], raw Yat scalars (softplus is applied here);
+ *                required for ATTN_YAT, ignored otherwise (may be NULL).
+ *                b_raw = -inf gives the bias-free kernel b = 0.
+ * log_tau        device fp32 [Hq]; required for ATTN_STAU, else ignored.
+ * causal         nonzero: key j is allowed for query i iff j <= i.
+ * mass,          device fp32 [B,Hq,Tq], contiguous; NULL means "do not
+ * max_score      store" (they are computed regardless).
+ * workspace      device memory of at least attn_fwd_workspace_bytes() bytes,
+ *                16-byte aligned; may be NULL when that size is 0.  Its
+ *                contents on entry do not matter; it is overwritten.
+ * stream         a hipStream_t (NULL = the null stream).
+ *
+ * Ownership: the caller owns every buffer; the library allocates no device
+ * or host memory per call.  The call only validates and enqueues work on
+ * `stream`; it returns before the work finishes, and device-side faults
+ * surface at the caller's next synchronisation.  On any error nothing is
+ * enqueued and no output is written.  Calls on different streams that share
+ * a workspace race.  B == 0 or T_q == 0 is a valid empty problem: nothing is
+ * enqueued and ATTN_OK is returned. */
+int attn_fwd(const attn_desc* desc, const void* q, const void* k, const void* v, int variant,
+             const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
+             void* out, float* mass, float* max_score, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Text of the most recent ATTN_ERR_HIP (or validation detail) on the calling
+ * thread; "" if none. */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFS_ATTN_H */

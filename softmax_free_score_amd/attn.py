@@ -1,0 +1,165 @@
+"""ctypes binding of ``libsfs_attn.so`` (the C ABI in ``include/sfs_attn.h``).
+
+Argument marshalling only: shapes, strides and device pointers of torch
+tensors go in, the library validates and enqueues the kernels on the current
+HIP stream.  Every step of the attention forward runs in the library; there is
+no fallback -- without the built library every call raises.
+
+    out, mass, max_score = attn_fwd(q, k, v, "yat", b_raw=..., eps_raw=...,
+                                    causal=True)
+
+q [B,Hq,Tq,dk], k [B,Hkv,Tk,dk], v [B,Hkv,Tk,dv] and out [B,Hq,Tq,dv] are
+device tensors of one dtype (bfloat16 or float32) whose last axis is
+contiguous; any strides on the other axes that are multiples of 16 bytes are
+accepted.  b_raw, eps_raw and log_tau are float32 [Hq] device tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfs_attn.so")
+
+ATTN_SOFTMAX, ATTN_YAT, ATTN_STAU = 0, 1, 2
+ATTN_F32, ATTN_BF16 = 0, 1
+VARIANTS = {"softmax": ATTN_SOFTMAX, "yat": ATTN_YAT, "stau": ATTN_STAU}
+STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
+          -4: "ATTN_ERR_PARAM", -5: "ATTN_ERR_WORKSPACE", -6: "ATTN_ERR_HIP"}
+EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_status_string",
+           "attn_last_error")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("Tq", ctypes.c_int64), ("Tk", ctypes.c_int64), ("dk", ctypes.c_int64),
+                ("dv", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Open the built library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m softmax_free_score_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.attn_desc_init.argtypes = [ctypes.POINTER(AttnDesc), i64, i64, i64, i64, i64, i64,
+                                       i64, ctypes.c_int32]
+        lib.attn_desc_init.restype = ctypes.c_int
+        lib.attn_fwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+        lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, ctypes.c_int, vp, vp, vp,
+                                 ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_status_string.argtypes = [ctypes.c_int]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_desc(q, k, v, out=None) -> AttnDesc:
+    """Descriptor from 4-D tensors (strides in elements, last axis contiguous)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t is None:
+            continue
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, T, d]")
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} needs a contiguous last axis")
+    B, Hq, Tq, dk = q.shape
+    Hkv, Tk, dv = v.shape[1], v.shape[2], v.shape[3]
+    if k.shape != (B, Hkv, Tk, dk) or v.shape[0] != B:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    d = AttnDesc()
+    d.B, d.Hq, d.Hkv, d.Tq, d.Tk, d.dk, d.dv = B, Hq, Hkv, Tq, Tk, dk, dv
+    d.dtype = _dtype_code(q)
+    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        if t is not None:
+            getattr(d, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return d
+
+
+def workspace_bytes(q, k, v, variant) -> int:
+    return int(load_library().attn_fwd_workspace_bytes(ctypes.byref(make_desc(q, k, v)),
+                                                       VARIANTS.get(variant, variant)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False, out=None,
+             mass=None, max_score=None, workspace=None, stream=None):
+    """Enqueue the fused forward; returns (out, mass, max_score).
+
+    Outputs that are not given are allocated (out like q with d_v columns;
+    mass and max_score float32 [B,Hq,Tq]); a workspace of the required size is
+    allocated when not given.  ``stream`` defaults to torch's current stream
+    on q's device.  Raises AttnError with the library's status on failure."""
+    lib = load_library()
+    variant = VARIANTS.get(variant, variant)
+    B, Hq, Tq, _ = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, Hq, Tq, dv), dtype=q.dtype, device=q.device)
+    if mass is None:
+        mass = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if max_score is None:
+        max_score = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    for name, t in (("mass", mass), ("max_score", max_score)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.numel() != B * Hq * Tq):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of B*Hq*Tq elements")
+    desc = make_desc(q, k, v, out)
+    need = int(lib.attn_fwd_workspace_bytes(ctypes.byref(desc), variant))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    st = lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), variant, _ptr(b_raw),
+                      _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(out), _ptr(mass),
+                      _ptr(max_score), _ptr(workspace), ws_bytes,
+                      ctypes.c_void_p(stream) if stream else None)
+    if st != 0:
+        raise AttnError(st, lib.attn_last_error().decode())
+    return out, mass, max_score
+
+
+def call_raw(desc: AttnDesc, q, k, v, variant, b_raw, eps_raw, log_tau, causal, out, mass,
+             max_score, workspace, workspace_bytes, stream) -> int:
+    """The C entry point with raw integer pointers (0 = NULL); returns the status."""
+    lib = load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    dp = ctypes.byref(desc) if desc is not None else None
+    return int(lib.attn_fwd(dp, p(q), p(k), p(v), int(variant), p(b_raw),
+                            p(eps_raw), p(log_tau), int(causal), p(out), p(mass), p(max_score),
+                            p(workspace), int(workspace_bytes), p(stream)))

@@ -1,0 +1,199 @@
+// attn_api.cpp -- the C ABI declared in include/sfs_attn.h.
+//
+// Every argument is validated on the host before any HIP call, so a bad call
+// returns its status code, enqueues nothing and writes nothing -- also on a
+// machine without a GPU.  The library allocates nothing per call.
+#include "sfs_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "attn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* msg) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+}
+
+bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks one tensor's strides: non-negative multiples of 16 bytes, and the
+// byte span of one (batch, head) slice below 2^31 (kernels use 32-bit offsets
+// inside a slice).
+bool strides_ok(const int64_t s[3], int64_t rows, int64_t d, int64_t elem) {
+  const int64_t align = 16 / elem;
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || s[i] % align != 0) return false;
+  if (s[2] < d) return false;  // rows of one slice may not overlap
+  const int64_t span = ((rows - 1) * s[2] + d) * elem;
+  return span < (int64_t(1) << 31);
+}
+
+int validate(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
+             const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
+             const void* out, const float* mass, const float* max_score, const void* ws,
+             size_t ws_bytes, bool* empty) {
+  *empty = false;
+  if (!d) {
+    set_error("desc is NULL");
+    return ATTN_ERR_NULL;
+  }
+  if (d->B < 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq < 0 || d->Tk <= 0 || d->dk <= 0 ||
+      d->dv <= 0) {
+    set_error("a size is out of range (B >= 0, Hq, Hkv >= 1, Tq >= 0, Tk >= 1, dk, dv >= 1)");
+    return ATTN_ERR_SHAPE;
+  }
+  if (d->Hq % d->Hkv != 0) {
+    set_error("Hq must be a multiple of Hkv");
+    return ATTN_ERR_SHAPE;
+  }
+  if (causal && d->Tq != d->Tk) {
+    set_error("a causal mask needs Tq == Tk");
+    return ATTN_ERR_SHAPE;
+  }
+  if (d->B > INT32_MAX || d->Hq > INT32_MAX || d->Tq > INT32_MAX || d->Tk > INT32_MAX ||
+      d->B * d->Hq * d->Tq > INT32_MAX) {
+    set_error("problem too large for 32-bit row indices");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (variant < ATTN_SOFTMAX || variant > ATTN_STAU) {
+    set_error("unknown variant");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (d->dtype != ATTN_F32 && d->dtype != ATTN_BF16) {
+    set_error("unknown dtype");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (!head_dim_ok(d->dk) || !head_dim_ok(d->dv)) {
+    set_error("dk and dv must be 16, 32, 64 or 128");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (d->B == 0 || d->Tq == 0) {
+    *empty = true;
+    return ATTN_OK;
+  }
+  if (!q || !k || !v || !out) {
+    set_error("q, k, v and out are required");
+    return ATTN_ERR_NULL;
+  }
+  if (variant == ATTN_YAT && (!b_raw || !eps_raw)) {
+    set_error("the Yat map needs b_raw and eps_raw");
+    return ATTN_ERR_PARAM;
+  }
+  if (variant == ATTN_STAU && !log_tau) {
+    set_error("the s^tau map needs log_tau");
+    return ATTN_ERR_PARAM;
+  }
+  const int64_t elem = d->dtype == ATTN_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(mass) & 3u) || (reinterpret_cast<uintptr_t>(max_score) & 3u)) {
+    set_error("q, k, v, out must be 16-byte aligned; mass and max_score 4-byte aligned");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (!strides_ok(d->q_stride, d->Tq, d->dk, elem) || !strides_ok(d->k_stride, d->Tk, d->dk, elem) ||
+      !strides_ok(d->v_stride, d->Tk, d->dv, elem) || !strides_ok(d->o_stride, d->Tq, d->dv, elem)) {
+    set_error("strides must be non-negative multiples of 16 bytes, row stride >= row width, "
+              "and one (batch, head) slice must span less than 2^31 bytes");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  const size_t need = attn_fwd_workspace_bytes(d, variant);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) {
+    set_error("workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()");
+    return ATTN_ERR_WORKSPACE;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_desc_init(attn_desc* d, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
+                   int64_t dk, int64_t dv, int32_t dtype) {
+  if (!d) return ATTN_ERR_NULL;
+  std::memset(d, 0, sizeof *d);
+  d->B = B; d->Hq = Hq; d->Hkv = Hkv; d->Tq = Tq; d->Tk = Tk; d->dk = dk; d->dv = dv;
+  d->dtype = dtype;
+  d->q_stride[2] = dk; d->q_stride[1] = Tq * dk; d->q_stride[0] = Hq * Tq * dk;
+  d->k_stride[2] = dk; d->k_stride[1] = Tk * dk; d->k_stride[0] = Hkv * Tk * dk;
+  d->v_stride[2] = dv; d->v_stride[1] = Tk * dv; d->v_stride[0] = Hkv * Tk * dv;
+  d->o_stride[2] = dv; d->o_stride[1] = Tq * dv; d->o_stride[0] = Hq * Tq * dv;
+  return ATTN_OK;
+}
+
+size_t attn_fwd_workspace_bytes(const attn_desc* d, int variant) {
+  if (!d || variant != ATTN_YAT || d->dtype != ATTN_BF16) return 0;
+  if (d->B <= 0 || d->Hkv <= 0 || d->Tk <= 0) return 0;
+  return (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * sizeof(float);
+}
+
+int attn_fwd(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
+             const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
+             void* out, float* mass, float* max_score, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  bool empty = false;
+  const int st = validate(d, q, k, v, variant, b_raw, eps_raw, log_tau, causal, out, mass,
+                          max_score, workspace, workspace_bytes, &empty);
+  if (st != ATTN_OK || empty) return st;
+
+  sfs::Problem p{};
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.mass = mass; p.max_score = max_score;
+  p.b_raw = b_raw; p.eps_raw = eps_raw; p.log_tau = log_tau;
+  p.nk = static_cast<float*>(workspace);
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = d->q_stride[i]; p.ks[i] = d->k_stride[i];
+    p.vs[i] = d->v_stride[i]; p.os[i] = d->o_stride[i];
+  }
+  p.B = (int)d->B; p.Hq = (int)d->Hq; p.Hkv = (int)d->Hkv;
+  p.Tq = (int)d->Tq; p.Tk = (int)d->Tk; p.dk = (int)d->dk; p.dv = (int)d->dv;
+  p.variant = variant;
+  p.causal = causal ? 1 : 0;
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d->dtype == ATTN_F32) {
+      e = sfs::launch_f32(p, s);
+    } else {
+      switch (p.dk) {
+        case 16: e = sfs::launch_bf16_dk16(p, s); break;
+        case 32: e = sfs::launch_bf16_dk32(p, s); break;
+        case 64: e = sfs::launch_bf16_dk64(p, s); break;
+        default: e = sfs::launch_bf16_dk128(p, s); break;
+      }
+    }
+  }
+  if (e != hipSuccess) {
+    char msg[256];
+    std::snprintf(msg, sizeof msg, "HIP: %s (%s)", hipGetErrorName(e), hipGetErrorString(e));
+    set_error(msg);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, variant, head size, alignment or size";
+    case ATTN_ERR_PARAM: return "a per-head parameter the variant needs is NULL";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,479 @@
+// attn_bf16.hip -- fused attention forward for bf16 storage on gfx950.
+//
+// Compiled once per key width: -DSFS_DK=16|32|64|128.  Each translation unit
+// holds the |k|^2 pre-pass for that width and the fused kernel for the three
+// score-to-weight maps x four value widths.
+//
+// What is computed (per batch b, query head h, query row i; h_kv = h / g):
+//   Yat     ("Softmax-Free Attention in JAX/Flax NNX", "One module, two
+//            compatibility functions"): kappa = (q.k + b)^2 /
+//            (max(|q|^2 + |k|^2 - 2 q.k, 0) + eps), masked kappa = 0,
+//            out = sum kappa v / (sum kappa + 1e-9).
+//   softmax ("NNX Scaled Dot-Product Attention", displayed equation):
+//            softmax(q.k / sqrt(d_k)) with -inf on blocked keys.
+//   s^tau   ("s^tau" forum post, core formula): phi = softplus(s) + 1e-6,
+//            w = phi^tau / sum phi^tau, tau = softplus(log_tau) + 1.
+//
+// Design (gfx950 / CDNA4, wave64):
+//   * A workgroup owns BM = 32*NW query rows of one (b, h); wave w owns 32.
+//     Its queries stay in registers as the B operand of the score MFMA.
+//   * Key/value tiles of BN rows stream HBM -> registers -> LDS.  K is kept
+//     row-major, V is transposed on the way in (V^T, keys contiguous), since
+//     the value MFMA contracts over keys and wants 8 consecutive keys per lane.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16: lane (half, col) then holds query col and 16
+//     keys, so the score accumulator is already the B operand of the value
+//     MFMA O^T = V^T P^T after an in-register bf16 conversion.  K rows are
+//     written to LDS with bits 2 and 3 of the row index swapped; with that,
+//     accumulator element r of 32-key block kb is key 32kb + 16(r/8) + 8 half
+//     + r%8, i.e. eight consecutive keys per half per k-step of the second
+//     MFMA, in natural order.
+//   * The Yat distance is built in registers from the same score tile:
+//     d2 = (|q|^2 + |k|^2) - 2 s.  |k|^2 comes from a pre-pass and |q|^2 from
+//     the workgroup's own query fragments; both use the same MFMA instruction
+//     and k-step order as the score tile (diagonals of X X^T), so for a key
+//     equal to its query the three terms cancel to exactly 0 and the peak
+//     (|q|^2 + b)^2 / eps is reproduced.
+//   * Yat and s^tau accumulate sum(p v) and the mass in one pass with no
+//     running maximum; softmax keeps an online maximum and rescales.
+//   * Row statistics are per-lane partials over the lane's keys, combined
+//     with the partner lane (lane ^ 32) once per tile (softmax maximum) or
+//     once at the end (mass, max_score).
+//   * Ragged tails: buffer loads past the end of a (b, h) slice return 0; the
+//     mask zeroes keys >= T_k; query rows >= T_q are computed but not stored.
+#include "attn_launch.h"
+
+#ifndef SFS_DK
+#error "compile with -DSFS_DK=16, 32, 64 or 128"
+#endif
+
+#define SFS_CAT2(a, b) a##b
+#define SFS_CAT(a, b) SFS_CAT2(a, b)
+
+namespace sfs {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Buffer-resource word 3 for raw (unformatted) dword access on gfx9.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;  // round to nearest even
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(unsigned, v);
+}
+// log(1 + e^x) without overflow (fp32 library calls; used once per head).
+__device__ __forceinline__ float softplus_precise(float x) {
+  return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+}
+// Byte size of a (b, h) slice with rows of `d` elements at `row_stride`.
+__device__ __forceinline__ uint32_t slice_bytes(int rows, int64_t row_stride, int d) {
+  return (uint32_t)(((int64_t)(rows - 1) * row_stride + d) * 2);
+}
+// Row position inside a 32-row block of the K tile in LDS: bits 2 and 3 swapped.
+__device__ __forceinline__ int k_lds_row(int j) {
+  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+// Diagonal of the 32x32 accumulator of X X^T: column n = col sits in the lane
+// half (col >> 2) & 1, element 4 (col >> 3) + (col & 3).
+__device__ __forceinline__ bool holds_diag(int col, int half) { return ((col >> 2) & 1) == half; }
+__device__ __forceinline__ float diag_of(const f32x16& g, int col) {
+  const int r = 4 * (col >> 3) + (col & 3);
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d = (i == r) ? g[i] : d;
+  return d;
+}
+
+// |k_j|^2 for every key row, by the same MFMA sequence as the score tile.
+// One wave per 32 rows; grid (ceil(T/128), H, B), 256 threads.
+template <int DK>
+__global__ __launch_bounds__(256) void row_norms_bf16(const unsigned short* x, int64_t s0,
+                                                      int64_t s1, int64_t s2, int H, int T,
+                                                      float* out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int row = blockIdx.x * 128 + 32 * w + col;
+  const unsigned short* base = x + (int64_t)b * s0 + (int64_t)h * s1;
+  const uint32_t bytes = slice_bytes(T, s2, DK);
+  const rsrc_t r = make_rsrc(base, bytes);
+  const uint32_t off = row < T ? (uint32_t)(((int64_t)row * s2 + 8 * half) * 2) : bytes;
+  f32x16 g = {};
+#pragma unroll
+  for (int s = 0; s < DK / 16; ++s)
+    g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
+               __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
+  if (row < T && holds_diag(col, half))
+    out[((int64_t)b * H + h) * nk_pitch(T) + row] = diag_of(g, col);
+}
+
+template <int VAR, int DK, int DV, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
+  constexpr int BM = NW * 32;            // query rows per workgroup
+  constexpr int NT = NW * 64;            // threads
+  constexpr int KS = DK / 16;            // k-steps of the score MFMA
+  constexpr int DVP = DV < 32 ? 32 : DV; // value width padded to the MFMA block
+  constexpr int DB = DVP / 32;           // 32-row blocks of O^T
+  constexpr int KB = BN / 32;            // 32-key blocks per tile
+  constexpr int KLD = DK + 8;            // LDS pitch of K rows (bf16), padded
+  constexpr int VLD = BN + 8;            // LDS pitch of V^T rows (bf16), padded
+  constexpr int KCH = DK / 8;            // 16-byte chunks per K row
+  constexpr int K_UNITS = BN * KCH;
+  constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
+  constexpr int V_UNITS = (BN / 4) * (DV / 8);  // 4 keys x 8 values each
+  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) unsigned short sK[BN * KLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[DVP * VLD];
+  __shared__ __attribute__((aligned(16))) float sNK[BN];
+  __shared__ float sNQ[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  // Workgroup -> (query tile, batch, head).  Heads vary fastest; with a causal
+  // mask the longest query tiles are dispatched first.
+  const int n_qt = (p.Tq + BM - 1) / BM;
+  const int nbh = p.B * p.Hq;
+  int qt = blockIdx.x / nbh;
+  const int bh = blockIdx.x - qt * nbh;
+  if (p.causal) qt = n_qt - 1 - qt;
+  const int b = bh / p.Hq, h = bh - b * p.Hq;
+  const int hk = h / (p.Hq / p.Hkv);
+  const int q0 = qt * BM, qw = q0 + 32 * w, my_q = qw + col;
+
+  const unsigned short* qbase =
+      (const unsigned short*)p.q + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[1];
+  const unsigned short* kbase =
+      (const unsigned short*)p.k + (int64_t)b * p.ks[0] + (int64_t)hk * p.ks[1];
+  const unsigned short* vbase =
+      (const unsigned short*)p.v + (int64_t)b * p.vs[0] + (int64_t)hk * p.vs[1];
+  const uint32_t q_bytes = slice_bytes(p.Tq, p.qs[2], DK);
+  const uint32_t k_bytes = slice_bytes(p.Tk, p.ks[2], DK);
+  const uint32_t v_bytes = slice_bytes(p.Tk, p.vs[2], DV);
+  const rsrc_t rq = make_rsrc(qbase, q_bytes);
+  const rsrc_t rk = make_rsrc(kbase, k_bytes);
+  const rsrc_t rv = make_rsrc(vbase, v_bytes);
+  const int kst = (int)p.ks[2], vst = (int)p.vs[2];
+
+  // Per-head scalars (prologue).
+  float bias = 0.f, eps = 0.f, tau = 0.f;
+  if (VAR == kYat) {
+    bias = softplus_precise(p.b_raw[h]);
+    eps = softplus_precise(p.eps_raw[h]);
+  } else if (VAR == kStau) {
+    tau = softplus_precise(p.log_tau[h]) + 1.f;
+  }
+  const float scale = 1.0f / sqrtf((float)DK);
+
+  // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7].
+  bf16x8 qf[KS];
+  {
+    const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
+                                     : q_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
+  }
+  float nq = 0.f;
+  // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
+  // tile never reads past it (entries >= T_k are masked out).
+  const float* nk_slice =
+      VAR == kYat ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+  if (VAR == kYat) {
+    f32x16 g = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
+    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
+    __syncthreads();
+    nq = sNQ[32 * w + col];
+  }
+
+  const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  // Staging registers for the next key/value tile.
+  u32x4 kreg[K_PER_T];
+  u32x4 vreg[V_PER_T][4];
+  u32x4 nkreg = {0u, 0u, 0u, 0u};
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < K_UNITS) {
+        const int row = k0 + u / KCH, c = u % KCH;
+        const uint32_t off = row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes;
+        kreg[i] = ld128(rk, off);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < V_UNITS) {
+        const int g4 = u % (BN / 4), c = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = k0 + 4 * g4 + r;
+          const uint32_t off = row < p.Tk ? (uint32_t)((row * vst + 8 * c) * 2) : v_bytes;
+          vreg[i][r] = ld128(rv, off);
+        }
+      }
+    }
+    if (VAR == kYat && tid < BN / 4) nkreg = *(const u32x4*)(nk_slice + k0 + 4 * tid);
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < K_UNITS) {
+        const int j = u / KCH, c = u % KCH;
+        const int row = (j & ~31) | k_lds_row(j & 31);
+        *(u32x4*)&sK[row * KLD + 8 * c] = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < V_UNITS) {
+        const int g4 = u % (BN / 4), c = u / (BN / 4);
+        // 4 keys x 8 values -> 8 value rows of 4 keys each.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
+          const unsigned a2 = vreg[i][2][e], a3 = vreg[i][3][e];
+          u32x2 lo, hi;
+          lo[0] = (a0 & 0xffffu) | (a1 << 16);
+          lo[1] = (a2 & 0xffffu) | (a3 << 16);
+          hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+          hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+          *(u32x2*)&sV[(8 * c + 2 * e) * VLD + 4 * g4] = lo;
+          *(u32x2*)&sV[(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
+        }
+      }
+    }
+    if (VAR == kYat && tid < BN / 4) *(u32x4*)&sNK[4 * tid] = nkreg;
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x16{};
+  float mass = 0.f;        // Yat, s^tau: sum of weights; softmax: sum exp2(x - m2)
+  float mx = -INFINITY;    // Yat: max kappa; s^tau: max s; softmax: running max of x
+  const float c_sm = scale * kLog2e;
+
+  load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(k0 + BN);
+    if (p.causal && k0 > qw + 31) continue;  // every key of the tile is in this wave's future
+    const bool need_mask = (p.causal && k0 + BN - 1 > qw) || (k0 + BN > p.Tk);
+
+    // S^T = K Q^T.
+    f32x16 sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, *(const u32x4*)&sK[(kb * 32 + col) * KLD + 16 * s + 8 * half]);
+        sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+      }
+    }
+
+    // Score -> weight, in registers.
+    if (VAR == kSoftmax) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kb][r] * c_sm;
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+            if ((p.causal && key > my_q) || key >= p.Tk) x = -INFINITY;
+          }
+          sacc[kb][r] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (tmax > mx) {
+        const float alpha = exp2f(mx - tmax);  // mx = -inf on the first tile: alpha = 0
+        mass *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) o[d] *= alpha;
+        mx = tmax;
+      }
+      const float mref = mx == -INFINITY ? 0.f : mx;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(sacc[kb][r] - mref);
+          sacc[kb][r] = e;
+          mass += e;
+        }
+    } else if (VAR == kYat) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 n0 = *(const u32x4*)&sNK[kb * 32 + 8 * half];
+        const u32x4 n1 = *(const u32x4*)&sNK[kb * 32 + 8 * half + 4];
+        const u32x4 n2 = *(const u32x4*)&sNK[kb * 32 + 16 + 8 * half];
+        const u32x4 n3 = *(const u32x4*)&sNK[kb * 32 + 16 + 8 * half + 4];
+        float nk[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nk[e] = __builtin_bit_cast(float, n0[e]);
+          nk[4 + e] = __builtin_bit_cast(float, n1[e]);
+          nk[8 + e] = __builtin_bit_cast(float, n2[e]);
+          nk[12 + e] = __builtin_bit_cast(float, n3[e]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sacc[kb][r];
+          const float d2 = fmaf(-2.f, s, nq + nk[r]);
+          const float u = s + bias;
+          float kap = u * u * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+            if ((p.causal && key > my_q) || key >= p.Tk) kap = 0.f;
+          }
+          sacc[kb][r] = kap;
+          mass += kap;
+          mx = fmaxf(mx, kap);
+        }
+      }
+    } else {  // s^tau
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sacc[kb][r] * scale;
+          const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+          const float sp = fmaf(__builtin_amdgcn_logf(1.f + e), kLn2, fmaxf(s, 0.f));
+          float u = __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(sp + 1e-6f));
+          bool allowed = true;
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+            allowed = !((p.causal && key > my_q) || key >= p.Tk);
+          }
+          u = allowed ? u : 0.f;
+          sacc[kb][r] = u;
+          mass += u;
+          mx = allowed ? fmaxf(mx, s) : mx;
+        }
+    }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 pw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)&sV[(32 * d + col) * VLD + kb * 32 + 16 * s + 8 * half]);
+          o[d] = mfma32(a, pb, o[d]);
+        }
+      }
+  }
+
+  // Epilogue: combine the two lanes that share a query, normalise, store.
+  const float mass_all = mass + __shfl_xor(mass, 32);
+  const float mx_all = fmaxf(mx, __shfl_xor(mx, 32));
+  float inv;
+  if (VAR == kYat) inv = 1.f / (mass_all + 1e-9f);
+  else if (VAR == kSoftmax) inv = 1.f / mass_all;
+  else inv = mass_all > 0.f ? 1.f / mass_all : 0.f;
+  if (my_q < p.Tq) {
+    unsigned short* orow = (unsigned short*)p.out + (int64_t)b * p.os[0] +
+                           (int64_t)h * p.os[1] + (int64_t)my_q * p.os[2];
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dv0 = 32 * d + 8 * g4 + 4 * half;
+        if (dv0 < DV) {
+          u32x2 st;
+          st[0] = pack_bf16(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv);
+          st[1] = pack_bf16(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv);
+          *(u32x2*)&orow[dv0] = st;
+        }
+      }
+    if (half == 0) {
+      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
+      if (p.mass) p.mass[ri] = mass_all;
+      if (p.max_score) p.max_score[ri] = VAR == kSoftmax ? mx_all * kLn2 : mx_all;
+    }
+  }
+}
+
+template <int VAR, int DV>
+hipError_t launch_variant(const Problem& p, hipStream_t stream) {
+  constexpr int DK = SFS_DK;
+  constexpr int NW = 4;
+  constexpr int BN = 64;
+  if (VAR == kYat) {
+    const dim3 grid((p.Tk + 127) / 128, p.Hkv, p.B);
+    hipLaunchKernelGGL(row_norms_bf16<DK>, grid, dim3(256), 0, stream,
+                       (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk, p.nk);
+  }
+  const int n_qt = (p.Tq + NW * 32 - 1) / (NW * 32);
+  const unsigned n_wg = (unsigned)n_qt * (unsigned)p.B * (unsigned)p.Hq;
+  hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, NW, BN>), dim3(n_wg), dim3(NW * 64), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+template <int VAR>
+hipError_t launch_dv(const Problem& p, hipStream_t stream) {
+  switch (p.dv) {
+    case 16: return launch_variant<VAR, 16>(p, stream);
+    case 32: return launch_variant<VAR, 32>(p, stream);
+    case 64: return launch_variant<VAR, 64>(p, stream);
+    case 128: return launch_variant<VAR, 128>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t SFS_CAT(launch_bf16_dk, SFS_DK)(const Problem& p, hipStream_t stream) {
+  switch (p.variant) {
+    case kSoftmax: return launch_dv<kSoftmax>(p, stream);
+    case kYat: return launch_dv<kYat>(p, stream);
+    case kStau: return launch_dv<kStau>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sfs

@@ -1,0 +1,97 @@
+"""Helpers for GPU-vs-oracle parity: device upload of seeded inputs, one call
+through the C ABI, and the tolerance checks.
+
+Tolerances (fixed here, derived from the stated bar):
+  fp32 storage: out max|d| <= 1e-5 * max|ref| (normwise over the tensor);
+                mass |d| <= 1e-5 * |ref| per row;
+                max_score |d| <= 1e-5 * |ref| + 1e-6 * max|ref| per row.
+  bf16 storage: out max|d| <= 2e-2 * rms(V) (the value scale);
+                mass |d| <= 1e-2 * |ref| per row;
+                max_score |d| <= 1e-2 * |ref| + 1e-3 * max|ref| per row.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from softmax_free_score_amd import attn
+
+TOL = {
+    "f32": dict(out=1e-5, mass=1e-5, mx=1e-5, mx_floor=1e-6),
+    "bf16": dict(out=2e-2, mass=1e-2, mx=1e-2, mx_floor=1e-3),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(inp, tied_copy=True):
+    """Device tensors (q, k, v, params) holding exactly the oracle's values."""
+    dev = torch.device("cuda:0")
+    if inp.wl.dtype == "bf16":
+        def t(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = t(inp.q_bits), t(inp.k_bits), t(inp.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (inp.q, inp.k, inp.v))
+    prm = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in inp.params().items()}
+    return q, k, v, prm
+
+
+def run_gpu(q, k, v, prm, variant, causal, **kw):
+    out, mass, mx = attn.attn_fwd(q, k, v, variant, causal=causal, **prm, **kw)
+    torch.cuda.synchronize()
+    return out, mass, mx
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def oracle_full(inp, variant, causal):
+    q, k, v = inp.f64()
+    return oracle.attn_fwd_np(q, k, v, variant, causal=causal,
+                              **{n: a.astype(np.float64) for n, a in inp.params().items()})
+
+
+def oracle_rows(inp, variant, causal, rows):
+    q, k, v = inp.f64()
+    return oracle.attn_fwd_c(q, k, v, variant, causal=causal, rows=rows,
+                             **{n: a.astype(np.float64) for n, a in inp.params().items()})
+
+
+def check(dtype, got, ref, v_scale, label=""):
+    """got, ref: (out, mass, max_score) as float64 arrays of equal shape."""
+    tol = TOL[dtype]
+    out_g, mass_g, mx_g = got
+    out_r, mass_r, mx_r = ref
+    assert np.all(np.isfinite(out_g)) and np.all(np.isfinite(mass_g)) and np.all(np.isfinite(mx_g)), \
+        f"{label}: non-finite GPU output"
+    d_out = np.abs(out_g - out_r).max() if out_r.size else 0.0
+    scale = v_scale if dtype == "bf16" else max(np.abs(out_r).max(), 1e-30)
+    e_out = d_out / scale
+    e_mass = (np.abs(mass_g - mass_r) / np.maximum(np.abs(mass_r), 1e-30)).max()
+    mx_bound = tol["mx"] * np.abs(mx_r) + tol["mx_floor"] * np.abs(mx_r).max()
+    e_mx = (np.abs(mx_g - mx_r) / np.maximum(mx_bound, 1e-30)).max()
+    say(f"  {label}: out err {e_out:.3e} (tol {tol['out']:.0e}), mass rel err {e_mass:.3e} "
+        f"(tol {tol['mass']:.0e}), max_score err/bound {e_mx:.3f}")
+    assert e_out <= tol["out"], f"{label}: out error {e_out:.3e} > {tol['out']}"
+    assert e_mass <= tol["mass"], f"{label}: mass error {e_mass:.3e} > {tol['mass']}"
+    assert e_mx <= 1.0, f"{label}: max_score outside bound (ratio {e_mx:.3f})"
+    return e_out, e_mass
+
+
+def sample_rows(B, Hq, Tq, n_random=256, seed=123):
+    """Flat row ids: corners, tile edges and a seeded random set."""
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, Tq - 2, Tq - 1]
+    rows = set()
+    for i in edges:
+        if 0 <= i < Tq:
+            rows.add(i)                                   # b = 0, h = 0
+            rows.add(((B - 1) * Hq + Hq - 1) * Tq + i)    # last b, last h
+    rows.update(rng.integers(0, B * Hq * Tq, n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

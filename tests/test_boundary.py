@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad calls with the documented status before touching
+the device.  Pointers here are fake (never dereferenced: validation fails, or
+no device is present, before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from softmax_free_score_amd import attn
+
+HEADER = os.path.join(ROOT, "include", "sfs_attn.h")
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_PARAM, ERR_WS, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+A, K, V, O, BR, ER, LT, M, X, W = (0x10000 * i for i in range(1, 11))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(attn_\w+)\s*\(", text, flags=re.M))
+
+
+def test_library_exports_every_declared_function():
+    lib = attn.load_library()
+    declared = header_functions()
+    assert declared == set(attn.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def desc(B=1, Hq=2, Hkv=1, Tq=64, Tk=64, dk=64, dv=64, dtype=attn.ATTN_BF16):
+    d = attn.AttnDesc()
+    assert attn.load_library().attn_desc_init(ctypes.byref(d), B, Hq, Hkv, Tq, Tk, dk, dv,
+                                              dtype) == OK
+    return d
+
+
+def call(d, variant=attn.ATTN_SOFTMAX, causal=1, q=A, k=K, v=V, out=O, b=BR, e=ER, lt=LT,
+         mass=M, mx=X, ws=W, ws_bytes=1 << 20):
+    return attn.call_raw(d, q, k, v, variant, b, e, lt, causal, out, mass, mx, ws, ws_bytes, 0)
+
+
+def test_desc_init_strides():
+    d = desc(B=2, Hq=4, Hkv=2, Tq=10, Tk=12, dk=32, dv=16)
+    assert list(d.q_stride) == [4 * 10 * 32, 10 * 32, 32]
+    assert list(d.k_stride) == [2 * 12 * 32, 12 * 32, 32]
+    assert list(d.v_stride) == [2 * 12 * 16, 12 * 16, 16]
+    assert list(d.o_stride) == [4 * 10 * 16, 10 * 16, 16]
+    assert attn.load_library().attn_desc_init(None, 1, 1, 1, 1, 1, 16, 16, 0) == ERR_NULL
+
+
+def test_null_pointers():
+    assert attn.call_raw(None, A, K, V, 0, 0, 0, 0, 0, O, 0, 0, 0, 0, 0) == ERR_NULL
+    for kw in ("q", "k", "v", "out"):
+        assert call(desc(), **{kw: 0}) == ERR_NULL
+
+
+@pytest.mark.parametrize("field,value", [("B", -1), ("Hq", 0), ("Hkv", 0), ("Tq", -1),
+                                         ("Tk", 0), ("dk", 0), ("dv", -2)])
+def test_bad_sizes(field, value):
+    d = desc()
+    setattr(d, field, value)
+    assert call(d, causal=0) == ERR_SHAPE
+
+
+def test_head_grouping_and_causal_shape():
+    assert call(desc(Hq=3, Hkv=2)) == ERR_SHAPE
+    assert call(desc(Tq=32, Tk=64), causal=1) == ERR_SHAPE
+
+
+def test_unsupported():
+    assert call(desc(dk=48)) == ERR_UNSUP
+    assert call(desc(dv=256)) == ERR_UNSUP
+    assert call(desc(dtype=7)) == ERR_UNSUP
+    assert call(desc(), variant=3) == ERR_UNSUP
+    assert call(desc(), q=A + 8) == ERR_UNSUP        # misaligned base
+    assert call(desc(), mass=M + 2) == ERR_UNSUP     # misaligned statistics
+    d = desc()
+    d.k_stride[2] = 68                               # 136 bytes: not a multiple of 16
+    assert call(d) == ERR_UNSUP
+    d = desc()
+    d.v_stride[2] = 32                               # rows overlap
+    assert call(d) == ERR_UNSUP
+    d = desc(Tq=70000, Tk=70000, dk=128)
+    d.q_stride[2] = 1 << 14                          # one slice spans >= 2^31 bytes
+    assert call(d) == ERR_UNSUP
+
+
+def test_missing_per_head_parameters():
+    assert call(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
+    assert call(desc(), variant=attn.ATTN_YAT, e=0) == ERR_PARAM
+    assert call(desc(), variant=attn.ATTN_STAU, lt=0) == ERR_PARAM
+
+
+def test_workspace_rules():
+    lib = attn.load_library()
+    d = desc(B=2, Hq=4, Hkv=2, Tq=100, Tk=100)
+    need = lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_YAT)
+    assert need == 2 * 2 * 128 * 4                   # |k|^2 rows padded to 64
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_SOFTMAX) == 0
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_STAU) == 0
+    assert lib.attn_fwd_workspace_bytes(None, attn.ATTN_YAT) == 0
+    assert call(d, variant=attn.ATTN_YAT, ws=0) == ERR_WS
+    assert call(d, variant=attn.ATTN_YAT, ws_bytes=need - 4) == ERR_WS
+    assert call(d, variant=attn.ATTN_YAT, ws=W + 4) == ERR_WS
+
+
+def test_empty_problem_is_a_no_op():
+    assert call(desc(B=0), q=0, k=0, v=0, out=0) == OK
+    assert call(desc(Tq=0, Tk=5), causal=0, q=0, k=0, v=0, out=0) == OK
+
+
+def test_valid_call_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert call(desc(), variant=attn.ATTN_SOFTMAX) == ERR_HIP
+    assert "hip" in attn.load_library().attn_last_error().decode().lower()
+
+
+def test_status_strings():
+    lib = attn.load_library()
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_PARAM, ERR_WS, ERR_HIP):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(99) == b"unknown status"

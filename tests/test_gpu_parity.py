@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.  Small and medium problems are compared element by
+element; the full-size workloads run in the benchmark's launch configuration
+and are compared on sampled rows that the oracle evaluates one by one."""
+import numpy as np
+import pytest
+import torch
+
+from parity import (check, oracle_full, oracle_rows, run_gpu, sample_rows, say, to_device,
+                    to_np)
+from softmax_free_score_amd.workloads import WORKLOADS, make_custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def v_rms(inp):
+    return float(np.sqrt(np.mean(inp.v.astype(np.float64) ** 2)))
+
+
+def full_check(inp, variant, causal, label):
+    say(f"[gpu] {label} {variant} causal={causal} shape B{inp.wl.B} Hq{inp.wl.Hq} "
+        f"Hkv{inp.wl.Hkv} Tq{inp.wl.Tq} Tk{inp.wl.Tk} dk{inp.wl.dk} dv{inp.wl.dv} {inp.wl.dtype}")
+    q, k, v, prm = to_device(inp)
+    got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal)]
+    ref = oracle_full(inp, variant, causal)
+    return check(inp.wl.dtype, got, ref, v_rms(inp), f"{label}/{variant}")
+
+
+# ---------------------------------------------------------------- small sizes
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_tiny_fp32(variant):
+    inp = make_inputs(WORKLOADS["tiny"])
+    full_check(inp, variant, True, "tiny")
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_gpt_small_full(variant):
+    inp = make_inputs(WORKLOADS["gpt_small"])
+    full_check(inp, variant, True, "gpt_small")
+
+
+def test_gpt_small_tied_yat():
+    # k := q puts the Yat peak (|q|^2 + b)^2 / eps on the diagonal
+    inp = make_inputs(WORKLOADS["gpt_small"], tied=True)
+    full_check(inp, "yat", True, "gpt_small_tied")
+
+
+MEDIUM = [
+    # B, Hq, Hkv, Tq, Tk, dk, dv, causal
+    (2, 4, 2, 333, 333, 128, 128, True),
+    (1, 2, 1, 200, 517, 64, 128, False),
+    (2, 3, 3, 130, 130, 32, 32, True),
+    (1, 4, 4, 97, 97, 16, 16, True),
+    (1, 2, 2, 150, 260, 128, 64, False),
+    (1, 2, 1, 70, 70, 16, 128, True),
+    (1, 2, 2, 65, 300, 128, 16, False),
+    (1, 2, 2, 257, 257, 64, 32, True),
+]
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", MEDIUM, ids=lambda s: "x".join(map(str, s)))
+def test_medium_shapes_bf16(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=7, qk_std=1.5)
+    full_check(inp, variant, causal, "medium")
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", [(1, 2, 1, 100, 100, 32, 64, True),
+                                   (2, 2, 2, 33, 90, 128, 16, False)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_medium_shapes_fp32(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "f32", causal, seed=8)
+    full_check(inp, variant, causal, "medium_f32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tied_medium_yat(dtype):
+    inp = make_custom(1, 3, 3, 300, 300, 128, 128, dtype, True, seed=9, qk_std=2.0, tied=True)
+    full_check(inp, "yat", True, "tied_medium")
+
+
+# --------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 1, 64, 64, True), (1, 2, 2, 1, 1, 32, 32, False),
+                                   (2, 2, 1, 1, 1000, 128, 128, False),
+                                   (1, 1, 1, 5, 3, 16, 32, False)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_degenerate_sizes(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    for dtype in ("bf16", "f32"):
+        inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, dtype, causal, seed=10)
+        full_check(inp, variant, causal, f"degenerate_{dtype}")
+
+
+def test_empty_batch_is_a_no_op():
+    from softmax_free_score_amd import attn
+    q = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    out, mass, mx = attn.attn_fwd(q, k, k, "softmax", causal=True)
+    assert out.shape == (0, 2, 16, 64)
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_strided_layout_and_null_statistics(variant):
+    # tensors stored as [B, T, H, d] and viewed as [B, H, T, d]
+    inp = make_custom(2, 4, 2, 150, 150, 64, 128, "bf16", True, seed=11)
+    q, k, v, prm = to_device(inp)
+    qs, ks, vs = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    assert qs.stride(2) == 4 * 64 and ks.stride(2) == 2 * 64
+    out_s = torch.empty((2, 150, 4, 128), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    from softmax_free_score_amd import attn
+    attn.attn_fwd(qs, ks, vs, variant, causal=True, out=out_s, **prm)
+    ref_out, ref_mass, ref_mx = run_gpu(q, k, v, prm, variant, True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, ref_out)
+    # no statistics requested: same output
+    out_n = torch.empty_like(ref_out)
+    lib = attn.load_library()
+    desc = attn.make_desc(q, k, v, out_n)
+    ws = torch.empty(max(attn.workspace_bytes(q, k, v, variant), 16), dtype=torch.uint8,
+                     device="cuda")
+    st = attn.call_raw(desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), attn.VARIANTS[variant],
+                       prm["b_raw"].data_ptr(), prm["eps_raw"].data_ptr(),
+                       prm["log_tau"].data_ptr(), 1, out_n.data_ptr(), 0, 0, ws.data_ptr(),
+                       ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lib.attn_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(out_n, ref_out)
+
+
+# ------------------------------------------------------------- invariances
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_causality_and_determinism(variant):
+    inp = make_custom(1, 2, 2, 384, 384, 128, 128, "bf16", True, seed=12)
+    q, k, v, prm = to_device(inp)
+    a = run_gpu(q, k, v, prm, variant, True)
+    b = run_gpu(q, k, v, prm, variant, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), "two identical calls differ"
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 200:] = -k2[:, :, 200:]
+    v2[:, :, 200:] = 3.0
+    c = run_gpu(q, k2, v2, prm, variant, True)
+    for x, y in zip(a, c):
+        assert torch.equal(x[:, :, :200], y[:, :, :200]), "a row saw a future key"
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_gqa_equals_repeated_kv(variant):
+    inp = make_custom(2, 8, 2, 200, 200, 64, 64, "bf16", True, seed=13)
+    q, k, v, prm = to_device(inp)
+    a = run_gpu(q, k, v, prm, variant, True)
+    b = run_gpu(q, k.repeat_interleave(4, dim=1).contiguous(),
+                v.repeat_interleave(4, dim=1).contiguous(), prm, variant, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_unit_values_give_weight_sums(variant):
+    inp = make_custom(1, 2, 2, 256, 256, 128, 32, "bf16", True, seed=14)
+    q, k, v, prm = to_device(inp)
+    v1 = torch.ones_like(v)
+    out, mass, _ = run_gpu(q, k, v1, prm, variant, True)
+    o = to_np(out)
+    if variant == "yat":
+        m = to_np(mass)[..., None]
+        expect = m / (m + 1e-9)
+    else:
+        expect = np.ones_like(o)
+    # weights are rounded to bf16 before the value contraction: 2^-8 relative
+    assert np.abs(o - expect).max() < 8e-3
+
+
+# ------------------------------------------------- full sizes, sampled rows
+
+FULL = [("long_yat", "yat", False), ("long_yat", "softmax", False), ("long_yat", "yat", True),
+        ("stau_gqa", "stau", False), ("cross", "softmax", False), ("cross", "yat", False),
+        ("cross", "stau", False), ("gpt_small", "yat", True)]
+
+
+@pytest.mark.parametrize("name,variant,tied", FULL, ids=lambda x: str(x))
+def test_full_size_sampled(name, variant, tied):
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl, tied=tied)
+    say(f"[gpu] full-size {name} tied={tied} {variant}")
+    q, k, v, prm = to_device(inp)
+    out, mass, mx = run_gpu(q, k, v, prm, variant, wl.causal)
+    rows = sample_rows(wl.B, wl.Hq, wl.Tq)
+    ref = oracle_rows(inp, variant, wl.causal, rows)
+    flat = lambda t, d: to_np(t).reshape(-1, d)[rows].reshape(-1) if d == 1 else \
+        to_np(t).reshape(-1, d)[rows]
+    got = (flat(out, wl.dv), flat(mass, 1), flat(mx, 1))
+    check(wl.dtype, got, ref, float(np.sqrt(np.mean(inp.v[0, 0].astype(np.float64) ** 2))),
+          f"{name}{'_tied' if tied else ''}/{variant}")
+    # properties over every row
+    m = mass.float()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(m).all()
+    assert (m > 0).all()
+    if variant == "softmax":
+        assert (m >= 0.999).all()   # the maximal key contributes exp(0) = 1
