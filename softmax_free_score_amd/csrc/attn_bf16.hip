@@ -61,6 +61,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
   // Staging registers for the next key/value tile.
   u32x4 kreg[K_PER_T];
   u32x4 vreg[V_PER_T][4];
-  u32x4 nkreg = {0u, 0u, 0u, 0u};
+  f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
 
   auto load_tile = [&](int k0) {
 #pragma unroll
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
         }
       }
     }
-    if (VAR == kYat && tid < BN / 4) nkreg = *(const u32x4*)(nk_slice + k0 + 4 * tid);
+    if (VAR == kYat && tid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
   };
 
   auto store_tile = [&]() {
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
         }
       }
     }
-    if (VAR == kYat && tid < BN / 4) *(u32x4*)&sNK[4 * tid] = nkreg;
+    if (VAR == kYat && tid < BN / 4) *(f32x4*)&sNK[4 * tid] = nkreg;
   };
 
   f32x16 o[DB];
@@ -340,17 +341,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
     } else if (VAR == kYat) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 n0 = *(const u32x4*)&sNK[kb * 32 + 8 * half];
-        const u32x4 n1 = *(const u32x4*)&sNK[kb * 32 + 8 * half + 4];
-        const u32x4 n2 = *(const u32x4*)&sNK[kb * 32 + 16 + 8 * half];
-        const u32x4 n3 = *(const u32x4*)&sNK[kb * 32 + 16 + 8 * half + 4];
+        // (read as float vectors: this compiler mis-evaluates a bit_cast of a
+        // single vector element)
+        const f32x4 n0 = *(const f32x4*)&sNK[kb * 32 + 8 * half];
+        const f32x4 n1 = *(const f32x4*)&sNK[kb * 32 + 8 * half + 4];
+        const f32x4 n2 = *(const f32x4*)&sNK[kb * 32 + 16 + 8 * half];
+        const f32x4 n3 = *(const f32x4*)&sNK[kb * 32 + 16 + 8 * half + 4];
         float nk[16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          nk[e] = __builtin_bit_cast(float, n0[e]);
-          nk[4 + e] = __builtin_bit_cast(float, n1[e]);
-          nk[8 + e] = __builtin_bit_cast(float, n2[e]);
-          nk[12 + e] = __builtin_bit_cast(float, n3[e]);
+          nk[e] = n0[e];
+          nk[4 + e] = n1[e];
+          nk[8 + e] = n2[e];
+          nk[12 + e] = n3[e];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -373,8 +376,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float s = sacc[kb][r] * scale;
+          // softplus(s) = max(s, 0) + log1p(e), e = exp(-|s|) in (0, 1].  The
+          // rounding error c of u = 1 + e is exact (u - 1 - e); log1p(e) =
+          // ln(u) - c/u to first order, and c/u = c within a relative e.
           const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
-          const float sp = fmaf(__builtin_amdgcn_logf(1.f + e), kLn2, fmaxf(s, 0.f));
+          const float u1 = 1.f + e;
+          const float c = (u1 - 1.f) - e;
+          const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
           float u = __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(sp + 1e-6f));
           bool allowed = true;
           if (need_mask) {

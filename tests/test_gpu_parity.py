@@ -14,7 +14,11 @@ pytestmark = pytest.mark.gpu
 
 
 def v_rms(inp):
-    return float(np.sqrt(np.mean(inp.v.astype(np.float64) ** 2)))
+    return float(np.sqrt(np.mean(np.square(inp.v, dtype=np.float64))))
+
+
+def v_max(inp):
+    return float(np.abs(inp.v).max())
 
 
 def full_check(inp, variant, causal, label):
@@ -23,7 +27,7 @@ def full_check(inp, variant, causal, label):
     q, k, v, prm = to_device(inp)
     got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal)]
     ref = oracle_full(inp, variant, causal)
-    return check(inp.wl.dtype, got, ref, v_rms(inp), f"{label}/{variant}")
+    return check(inp.wl.dtype, got, ref, v_max(inp), f"{label}/{variant}", v_rms=v_rms(inp))
 
 
 # ---------------------------------------------------------------- small sizes
@@ -197,8 +201,8 @@ def test_full_size_sampled(name, variant, tied):
     flat = lambda t, d: to_np(t).reshape(-1, d)[rows].reshape(-1) if d == 1 else \
         to_np(t).reshape(-1, d)[rows]
     got = (flat(out, wl.dv), flat(mass, 1), flat(mx, 1))
-    check(wl.dtype, got, ref, float(np.sqrt(np.mean(inp.v[0, 0].astype(np.float64) ** 2))),
-          f"{name}{'_tied' if tied else ''}/{variant}")
+    check(wl.dtype, got, ref, v_max(inp), f"{name}{'_tied' if tied else ''}/{variant}",
+          v_rms=v_rms(inp))
     # properties over every row
     m = mass.float()
     assert torch.isfinite(out.float()).all() and torch.isfinite(m).all()
