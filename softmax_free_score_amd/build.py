@@ -62,22 +62,29 @@ def _compile(hipcc, name, src, defs, verbose):
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, extra_defs=(), out: str | None = None,
+          obj_dir: str | None = None) -> str:
+    """Compile and link; ``extra_defs`` are added to every kernel unit (e.g.
+    ``-DSFS_NW=8`` to change the launch shape), ``out`` overrides the library
+    path."""
+    global OBJ
     hipcc = _hipcc()
+    OBJ = obj_dir or OBJ
     os.makedirs(OBJ, exist_ok=True)
-    units = _units()
+    units = [(n, s, d + list(extra_defs)) for n, s, d in _units()]
     jobs = jobs or min(len(units), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda u: _compile(hipcc, *u, verbose), units))
-    tmp = LIB + ".tmp"
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

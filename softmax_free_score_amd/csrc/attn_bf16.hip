@@ -15,11 +15,12 @@
 //            w = phi^tau / sum phi^tau, tau = softplus(log_tau) + 1.
 //
 // Design (gfx950 / CDNA4, wave64):
-//   * A workgroup owns BM = 32*NW query rows of one (b, h); wave w owns 32.
-//     Its queries stay in registers as the B operand of the score MFMA.
-//   * Key/value tiles of BN rows stream HBM -> registers -> LDS.  K is kept
-//     row-major, V is transposed on the way in (V^T, keys contiguous), since
-//     the value MFMA contracts over keys and wants 8 consecutive keys per lane.
+//   * A workgroup of 8 waves owns BM = 256 query rows of one (b, h); each wave
+//     owns 32 rows, whose query fragments stay in registers as the B operand
+//     of the score MFMA.  Key/value tiles of BN rows are staged HBM ->
+//     registers -> LDS once for all 8 waves.  K is kept row-major, V is
+//     transposed on the way in (V^T, keys contiguous), since the value MFMA
+//     contracts over keys and wants 8 consecutive keys per lane.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: lane (half, col) then holds query col and 16
 //     keys, so the score accumulator is already the B operand of the value
@@ -28,6 +29,9 @@
 //     accumulator element r of 32-key block kb is key 32kb + 16(r/8) + 8 half
 //     + r%8, i.e. eight consecutive keys per half per k-step of the second
 //     MFMA, in natural order.
+//   * The two halves of the workgroup run a "ping-pong" schedule (see the
+//     kernel): on each SIMD one wave issues the matrix-core work of a tile
+//     while its partner maps the previous scores to weights on the vector ALU.
 //   * The Yat distance is built in registers from the same score tile:
 //     d2 = (|q|^2 + |k|^2) - 2 s.  |k|^2 comes from a pre-pass and |q|^2 from
 //     the workgroup's own query fragments; both use the same MFMA instruction
@@ -35,13 +39,17 @@
 //     equal to its query the three terms cancel to exactly 0 and the peak
 //     (|q|^2 + b)^2 / eps is reproduced.
 //   * Yat and s^tau accumulate sum(p v) and the mass in one pass with no
-//     running maximum; softmax keeps an online maximum and rescales.
+//     running maximum; softmax keeps a reference maximum that moves only when
+//     a tile's maximum exceeds it by more than 2^8 (then O and the sum are
+//     rescaled).
 //   * Row statistics are per-lane partials over the lane's keys, combined
-//     with the partner lane (lane ^ 32) once per tile (softmax maximum) or
-//     once at the end (mass, max_score).
+//     with the partner lane (lane ^ 32, v_permlane32_swap) once per tile
+//     (softmax maximum) or once at the end (mass, max_score).
 //   * Ragged tails: buffer loads past the end of a (b, h) slice return 0; the
 //     mask zeroes keys >= T_k; query rows >= T_q are computed but not stored.
 #include "attn_launch.h"
+
+#include <type_traits>
 
 #ifndef SFS_DK
 #error "compile with -DSFS_DK=16, 32, 64 or 128"
@@ -128,10 +136,48 @@ __global__ __launch_bounds__(256) void row_norms_bf16(const unsigned short* x, i
     out[((int64_t)b * H + h) * nk_pitch(T) + row] = diag_of(g, col);
 }
 
-template <int VAR, int DK, int DV, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
+// Partner-lane exchange for row statistics: lanes l and l ^ 32 hold the same
+// query.  v_permlane32_swap hands every lane both halves' values.
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)s[0]), __builtin_bit_cast(float, (unsigned)s[1]));
+}
+
+// Softmax keeps exponentials relative to a reference maximum that is only
+// moved when a tile's maximum exceeds it by more than this (log2 units):
+// weights stay below 2^8 and most tiles skip the rescale of the accumulator.
+constexpr float kRescaleSlack = 8.0f;
+
+// Fused forward, "ping-pong" schedule.
+//
+// A workgroup has 8 waves in two groups of 4 (group g = wave / 4); wave w and
+// wave w + 4 share a SIMD.  Each wave owns 32 query rows; the workgroup owns
+// BM = 256 rows of one (b, h) and streams key/value tiles of BN rows once for
+// both groups.  The groups run half an iteration apart, separated by one
+// workgroup barrier per phase:
+//
+//   phase 2t   : group 0 M(t)      group 1 W(t-1)
+//   phase 2t+1 : group 0 W(t)      group 1 M(t)
+//
+// M(t) is matrix-core work -- O += V_{t-1}^T P_{t-1}^T and S_t = K_t Q^T --
+// plus this group's share of the tile staging; W(t) is the score -> weight map
+// of S_t on the vector ALU.  On every SIMD one wave therefore issues MFMAs
+// while its partner issues VALU work.  Staging: group 0 writes K_{t+1} (and
+// its |k|^2 rows) in phase 2t, group 1 writes V_t in phase 2t+1; K and V are
+// double-buffered in LDS (K_t is read in phases 2t..2t+1, V_t in 2t+2..2t+3)
+// and the |k|^2 rows triple-buffered (read in W phases up to 2t+2).  Global
+// loads for a stage are issued one iteration before it is written.
+template <int VAR, int DK, int DV, int BN>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
+  constexpr int NW = 8;                  // waves per workgroup
   constexpr int BM = NW * 32;            // query rows per workgroup
-  constexpr int NT = NW * 64;            // threads
+  constexpr int GT = 256;                // threads per group
   constexpr int KS = DK / 16;            // k-steps of the score MFMA
   constexpr int DVP = DV < 32 ? 32 : DV; // value width padded to the MFMA block
   constexpr int DB = DVP / 32;           // 32-row blocks of O^T
@@ -140,16 +186,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
   constexpr int VLD = BN + 8;            // LDS pitch of V^T rows (bf16), padded
   constexpr int KCH = DK / 8;            // 16-byte chunks per K row
   constexpr int K_UNITS = BN * KCH;
-  constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
+  constexpr int K_PER_T = (K_UNITS + GT - 1) / GT;
   constexpr int V_UNITS = (BN / 4) * (DV / 8);  // 4 keys x 8 values each
-  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  constexpr int V_PER_T = (V_UNITS + GT - 1) / GT;
+  static_assert(BN % 32 == 0 && BN <= 64, "tiles are 32 or 64 keys");
 
-  __shared__ __attribute__((aligned(16))) unsigned short sK[BN * KLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sV[DVP * VLD];
-  __shared__ __attribute__((aligned(16))) float sNK[BN];
+  __shared__ __attribute__((aligned(16))) unsigned short sK[2][BN * KLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[2][DVP * VLD];
+  __shared__ __attribute__((aligned(16))) float sNK[3][BN];
   __shared__ float sNQ[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w >> 2, gtid = tid & (GT - 1);
   const int col = lane & 31, half = lane >> 5;
 
   // Workgroup -> (query tile, batch, head).  Heads vary fastest; with a causal
@@ -194,6 +242,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
                                      : q_bytes;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
+    // Drain these loads here: otherwise they are still outstanding on entry to
+    // the main loop, and every score MFMA there would wait for the tile loads
+    // issued after them.
+    __builtin_amdgcn_s_waitcnt(0);
   }
   float nq = 0.f;
   // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
@@ -205,31 +257,45 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
     if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
-    __syncthreads();
-    nq = sNQ[32 * w + col];
   }
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
 
-  // Staging registers for the next key/value tile.
+  // Staging registers: group 0 stages K (+ |k|^2), group 1 stages V.
   u32x4 kreg[K_PER_T];
   u32x4 vreg[V_PER_T][4];
   f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
 
-  auto load_tile = [&](int k0) {
+  auto load_k = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
-      const int u = tid + i * NT;
+      const int u = gtid + i * GT;
       if (u < K_UNITS) {
         const int row = k0 + u / KCH, c = u % KCH;
         const uint32_t off = row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes;
         kreg[i] = ld128(rk, off);
       }
     }
+    if (VAR == kYat && gtid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * gtid);
+  };
+  auto store_k = [&](int t) {
+    unsigned short* K = sK[t & 1];
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int u = gtid + i * GT;
+      if (u < K_UNITS) {
+        const int j = u / KCH, c = u % KCH;
+        const int row = (j & ~31) | k_lds_row(j & 31);
+        *(u32x4*)&K[row * KLD + 8 * c] = kreg[i];
+      }
+    }
+    if (VAR == kYat && gtid < BN / 4) *(f32x4*)&sNK[t % 3][4 * gtid] = nkreg;
+  };
+  auto load_v = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * NT;
+      const int u = gtid + i * GT;
       if (u < V_UNITS) {
         const int g4 = u % (BN / 4), c = u / (BN / 4);
 #pragma unroll
@@ -240,22 +306,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
         }
       }
     }
-    if (VAR == kYat && tid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
   };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (u < K_UNITS) {
-        const int j = u / KCH, c = u % KCH;
-        const int row = (j & ~31) | k_lds_row(j & 31);
-        *(u32x4*)&sK[row * KLD + 8 * c] = kreg[i];
-      }
-    }
+  auto store_v = [&](int t) {
+    unsigned short* Vt = sV[t & 1];
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * NT;
+      const int u = gtid + i * GT;
       if (u < V_UNITS) {
         const int g4 = u % (BN / 4), c = u / (BN / 4);
         // 4 keys x 8 values -> 8 value rows of 4 keys each.
@@ -268,45 +324,88 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
           lo[1] = (a2 & 0xffffu) | (a3 << 16);
           hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
           hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-          *(u32x2*)&sV[(8 * c + 2 * e) * VLD + 4 * g4] = lo;
-          *(u32x2*)&sV[(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
+          *(u32x2*)&Vt[(8 * c + 2 * e) * VLD + 4 * g4] = lo;
+          *(u32x2*)&Vt[(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
         }
       }
     }
-    if (VAR == kYat && tid < BN / 4) *(f32x4*)&sNK[4 * tid] = nkreg;
   };
 
   f32x16 o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
-  float mass = 0.f;        // Yat, s^tau: sum of weights; softmax: sum exp2(x - m2)
-  float mx = -INFINITY;    // Yat: max kappa; s^tau: max s; softmax: running max of x
+  f32x16 sacc[KB];          // S_t, from M(t) to W(t)
+  bf16x8 pb[KB][2];         // P_t in bf16, from W(t) to M(t+1)
+  float mass = 0.f;         // Yat, s^tau: sum of weights; softmax: sum exp2(x - mref)
+  float mx = -INFINITY;     // Yat: max kappa; s^tau: max s; softmax: max of x = s*log2e/sqrt(dk)
+  float mref = -INFINITY;   // softmax: reference maximum of the exponentials
   const float c_sm = scale * kLog2e;
 
-  load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int k0 = t * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(k0 + BN);
-    if (p.causal && k0 > qw + 31) continue;  // every key of the tile is in this wave's future
-    const bool need_mask = (p.causal && k0 + BN - 1 > qw) || (k0 + BN > p.Tk);
+  // wave has work on tile t unless all its keys lie in the wave's future
+  auto active = [&](int t) { return !(p.causal && t * BN > qw + 31); };
 
-    // S^T = K Q^T.
-    f32x16 sacc[KB];
+  // Matrix-core phases.  The A-operand fragments are read from LDS several
+  // MFMAs ahead of use (the issue order is pinned with scheduling groups), so
+  // the LDS latency is covered by MFMAs in flight instead of stalling each one.
+  auto qk = [&](int t) {
+    const unsigned short* K = sK[t & 1];
+    constexpr int NF = KS * KB;   // fragments, in use order (s major, kb minor)
+    constexpr int AHEAD = NF < 4 ? NF : 4;
+    bf16x8 fa[NF];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      sacc[kb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, *(const u32x4*)&sK[(kb * 32 + col) * KLD + 16 * s + 8 * half]);
-        sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-      }
+    for (int i = 0; i < NF; ++i) {
+      const int s = i / KB, kb = i % KB;
+      fa[i] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)&K[(kb * 32 + col) * KLD + 16 * s + 8 * half]);
     }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int s = i / KB, kb = i % KB;
+      sacc[kb] = mfma32(fa[i], qf[s], sacc[kb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NF - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+  };
+  auto pv = [&](int t) {
+    const unsigned short* Vt = sV[t & 1];
+    constexpr int NF = KB * 2 * DB;   // fragments, in use order ((kb, s) major, d minor)
+    constexpr int AHEAD = DB;
+    bf16x8 fa[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int ks = i / DB, d = i % DB, kb = ks >> 1, s = ks & 1;
+      fa[i] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)&Vt[(32 * d + col) * VLD + kb * 32 + 16 * s + 8 * half]);
+    }
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int ks = i / DB, d = i % DB, kb = ks >> 1, s = ks & 1;
+      o[d] = mfma32(fa[i], pb[kb][s], o[d]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NF - AHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+  };
 
-    // Score -> weight, in registers.
+  // Score -> weight for tile t (vector ALU only).
+  auto weights = [&](auto mask_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = t * BN;
+    auto allowed = [&](int kb, int r) {
+      const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+      return !((p.causal && key > my_q) || key >= p.Tk);
+    };
     if (VAR == kSoftmax) {
       float tmax = -INFINITY;
 #pragma unroll
@@ -314,22 +413,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = sacc[kb][r] * c_sm;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-            if ((p.causal && key > my_q) || key >= p.Tk) x = -INFINITY;
-          }
+          if (MASK) x = allowed(kb, r) ? x : -INFINITY;
           sacc[kb][r] = x;
           tmax = fmaxf(tmax, x);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      if (tmax > mx) {
-        const float alpha = exp2f(mx - tmax);  // mx = -inf on the first tile: alpha = 0
+      tmax = pair_max(tmax);
+      mx = fmaxf(mx, tmax);
+      if (tmax > mref + kRescaleSlack) {  // first tile: mref = -inf
+        const float alpha = __builtin_amdgcn_exp2f(mref - tmax);
         mass *= alpha;
 #pragma unroll
         for (int d = 0; d < DB; ++d) o[d] *= alpha;
-        mx = tmax;
+        mref = tmax;
       }
-      const float mref = mx == -INFINITY ? 0.f : mx;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -339,14 +435,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
           mass += e;
         }
     } else if (VAR == kYat) {
+      const float* NK = sNK[t % 3];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         // (read as float vectors: this compiler mis-evaluates a bit_cast of a
         // single vector element)
-        const f32x4 n0 = *(const f32x4*)&sNK[kb * 32 + 8 * half];
-        const f32x4 n1 = *(const f32x4*)&sNK[kb * 32 + 8 * half + 4];
-        const f32x4 n2 = *(const f32x4*)&sNK[kb * 32 + 16 + 8 * half];
-        const f32x4 n3 = *(const f32x4*)&sNK[kb * 32 + 16 + 8 * half + 4];
+        const f32x4 n0 = *(const f32x4*)&NK[kb * 32 + 8 * half];
+        const f32x4 n1 = *(const f32x4*)&NK[kb * 32 + 8 * half + 4];
+        const f32x4 n2 = *(const f32x4*)&NK[kb * 32 + 16 + 8 * half];
+        const f32x4 n3 = *(const f32x4*)&NK[kb * 32 + 16 + 8 * half + 4];
         float nk[16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -361,10 +458,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
           const float d2 = fmaf(-2.f, s, nq + nk[r]);
           const float u = s + bias;
           float kap = u * u * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-            if ((p.causal && key > my_q) || key >= p.Tk) kap = 0.f;
-          }
+          if (MASK) kap = allowed(kb, r) ? kap : 0.f;
           sacc[kb][r] = kap;
           mass += kap;
           mx = fmaxf(mx, kap);
@@ -377,26 +471,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
         for (int r = 0; r < 16; ++r) {
           const float s = sacc[kb][r] * scale;
           // softplus(s) = max(s, 0) + log1p(e), e = exp(-|s|) in (0, 1].  The
-          // rounding error c of u = 1 + e is exact (u - 1 - e); log1p(e) =
-          // ln(u) - c/u to first order, and c/u = c within a relative e.
+          // rounding error c of u1 = 1 + e is exact (u1 - 1 - e); log1p(e) =
+          // ln(u1) - c/u1 to first order, and c/u1 = c within a relative e.
           const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
           const float u1 = 1.f + e;
           const float c = (u1 - 1.f) - e;
           const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
           float u = __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(sp + 1e-6f));
-          bool allowed = true;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-            allowed = !((p.causal && key > my_q) || key >= p.Tk);
+          float sm = s;
+          if (MASK) {
+            const bool ok = allowed(kb, r);
+            u = ok ? u : 0.f;
+            sm = ok ? s : -INFINITY;
           }
-          u = allowed ? u : 0.f;
           sacc[kb][r] = u;
           mass += u;
-          mx = allowed ? fmaxf(mx, s) : mx;
+          mx = fmaxf(mx, sm);
         }
     }
-
-    // O^T += V^T P^T.
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -405,23 +497,60 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)&sV[(32 * d + col) * VLD + kb * 32 + 16 * s + 8 * half]);
-          o[d] = mfma32(a, pb, o[d]);
-        }
+        pb[kb][s] = __builtin_bit_cast(bf16x8, pw);
       }
+  };
+
+  // Prologue: K_0 into stage 0, K_1 and V_0 into the staging registers.
+  if (grp == 0) {
+    load_k(0);
+    store_k(0);
+    if (n_tiles > 1) load_k(BN);
+  } else {
+    load_v(0);
+  }
+  __syncthreads();
+  if (VAR == kYat) nq = sNQ[32 * w + col];
+
+  const int n_phases = 2 * n_tiles + 2;
+  for (int ph = 0; ph < n_phases; ++ph) {
+    const bool mphase = (ph & 1) == grp;
+    if (mphase) {
+      const int t = (ph - grp) >> 1;  // M(t)
+      // the matrix-core wave issues first; its VALU partner fills the gaps
+      __builtin_amdgcn_s_setprio(3);
+      if (t >= 1 && active(t - 1)) pv(t - 1);
+      if (t < n_tiles && active(t)) qk(t);
+      if (grp == 0) {
+        if (t + 1 < n_tiles) store_k(t + 1);
+        if (t + 2 < n_tiles) load_k((t + 2) * BN);
+      } else {
+        if (t < n_tiles) store_v(t);
+        if (t + 1 < n_tiles) load_v((t + 1) * BN);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      const int t = (ph - 1 - grp) >> 1;  // W(t)
+      if (t >= 0 && t < n_tiles && active(t)) {
+        const int k0 = t * BN;
+        const bool need_mask = (p.causal && k0 + BN - 1 > qw) || (k0 + BN > p.Tk);
+        if (need_mask) weights(std::true_type{}, t);
+        else weights(std::false_type{}, t);
+      }
+    }
+    __syncthreads();
   }
 
   // Epilogue: combine the two lanes that share a query, normalise, store.
-  const float mass_all = mass + __shfl_xor(mass, 32);
-  const float mx_all = fmaxf(mx, __shfl_xor(mx, 32));
+  float mass_all = pair_sum(mass);
+  const float mx_all = pair_max(mx);
+  if (VAR == kSoftmax) mass_all *= __builtin_amdgcn_exp2f(mref - mx_all);  // relative to the max
   float inv;
   if (VAR == kYat) inv = 1.f / (mass_all + 1e-9f);
   else if (VAR == kSoftmax) inv = 1.f / mass_all;
   else inv = mass_all > 0.f ? 1.f / mass_all : 0.f;
+  // softmax: O holds sum exp2(x - mref) v; mass_all is relative to mx_all
+  const float oscale = VAR == kSoftmax ? inv * __builtin_amdgcn_exp2f(mref - mx_all) : inv;
   if (my_q < p.Tq) {
     unsigned short* orow = (unsigned short*)p.out + (int64_t)b * p.os[0] +
                            (int64_t)h * p.os[1] + (int64_t)my_q * p.os[2];
@@ -432,8 +561,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
         const int dv0 = 32 * d + 8 * g4 + 4 * half;
         if (dv0 < DV) {
           u32x2 st;
-          st[0] = pack_bf16(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv);
-          st[1] = pack_bf16(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv);
+          st[0] = pack_bf16(o[d][4 * g4] * oscale, o[d][4 * g4 + 1] * oscale);
+          st[1] = pack_bf16(o[d][4 * g4 + 2] * oscale, o[d][4 * g4 + 3] * oscale);
           *(u32x2*)&orow[dv0] = st;
         }
       }
@@ -445,20 +574,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_bf16(Problem p) {
   }
 }
 
+// Keys per tile.
+#ifndef SFS_BN
+#define SFS_BN 64
+#endif
+
 template <int VAR, int DV>
 hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   constexpr int DK = SFS_DK;
-  constexpr int NW = 4;
-  constexpr int BN = 64;
+  constexpr int BN = SFS_BN;
+  constexpr int BM = 256;  // query rows per workgroup (8 waves)
   if (VAR == kYat) {
     const dim3 grid((p.Tk + 127) / 128, p.Hkv, p.B);
     hipLaunchKernelGGL(row_norms_bf16<DK>, grid, dim3(256), 0, stream,
                        (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk, p.nk);
   }
-  const int n_qt = (p.Tq + NW * 32 - 1) / (NW * 32);
+  const int n_qt = (p.Tq + BM - 1) / BM;
   const unsigned n_wg = (unsigned)n_qt * (unsigned)p.B * (unsigned)p.Hq;
-  hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, NW, BN>), dim3(n_wg), dim3(NW * 64), 0, stream,
-                     p);
+  hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(n_wg), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
