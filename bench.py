@@ -15,6 +15,7 @@ T(T+1)/2.  Durations are HIP events recorded on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +44,31 @@ def alg_bytes(wl) -> float:
     return float(q + kv + o + stats)
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "softmax_free_score_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, variant: str):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a
+    plain copy of known size), or None when there is none for this workload and
+    variant or the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(f"{workload}/{variant}")
+    if not r or r.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return r.get("bytes_per_launch")
+
+
 def time_calls(fn, stream, steps, warmup):
     """Average per-call duration (ms) by HIP events on `stream`, plus the
     wall time of the whole timed region."""
@@ -63,7 +89,7 @@ def time_calls(fn, stream, steps, warmup):
     return float(np.mean(per)), float(np.median(per)), wall
 
 
-def cpu_baseline(inp, variant, target_s=15.0):
+def cpu_baseline(inp, variant, target_s=25.0):
     """The fp64 C oracle on a strided sample of the query rows, timed on the
     host cores; scaled to TFLOP/s with the same algorithmic count."""
     import oracle
@@ -101,6 +127,9 @@ def main():
     ap.add_argument("--workload", default="long_yat")
     ap.add_argument("--variant", default="yat")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (the "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the attention "
@@ -158,7 +187,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": recorded_traffic(wl.name, primary),
+                     "traffic_unit": "bytes per launch of attn_fwd_bf16 (HBM, counters)",
                      "kernel": f"|k|^2 pre-pass + attn_fwd_bf16 ({primary}); flops = "
                                f"{flops:.4e} per launch ({wl.allowed_pairs} allowed pairs x "
                                f"2(dk+dv))",
@@ -171,6 +201,17 @@ def main():
     if "softmax" in others:
         # > 1 means the primary branch is faster than softmax on the same inputs
         line[f"{primary}_speed_vs_softmax"] = round(others["softmax"]["ms"] / mean_ms, 4)
+    line["roofline"]["alg_bytes_per_launch"] = alg_bytes(wl)
+    line["kernel_source_sha256_16"] = kernel_source_hash()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, primary)
     print(json.dumps(line), flush=True)
