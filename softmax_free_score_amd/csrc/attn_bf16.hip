@@ -452,16 +452,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           nk[8 + e] = n2[e];
           nk[12 + e] = n3[e];
         }
+        // In three stages over 8 elements (denominators, reciprocals,
+        // numerators) so that the reciprocals issue back to back instead of
+        // each stalling its own element.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s = sacc[kb][r];
-          const float d2 = fmaf(-2.f, s, nq + nk[r]);
-          const float u = s + bias;
-          float kap = u * u * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
-          if (MASK) kap = allowed(kb, r) ? kap : 0.f;
-          sacc[kb][r] = kap;
-          mass += kap;
-          mx = fmaxf(mx, kap);
+        for (int r0 = 0; r0 < 16; r0 += 8) {
+          float den[8], rc[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            den[r] = fmaxf(fmaf(-2.f, sacc[kb][r0 + r], nq + nk[r0 + r]), 0.f) + eps;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) rc[r] = __builtin_amdgcn_rcpf(den[r]);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const float u = sacc[kb][r0 + r] + bias;
+            float kap = u * u * rc[r];
+            if (MASK) kap = allowed(kb, r0 + r) ? kap : 0.f;
+            sacc[kb][r0 + r] = kap;
+            mass += kap;
+            mx = fmaxf(mx, kap);
+          }
         }
       }
     } else {  // s^tau
