@@ -127,6 +127,13 @@ def main():
     ap.add_argument("--workload", default="long_yat")
     ap.add_argument("--variant", default="yat")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-mib", type=int, default=0,
+                    help="cycle over enough distinct copies of the inputs and outputs to "
+                         "span this many MiB (larger than the 256 MB Infinity Cache, so "
+                         "small workloads are measured from HBM)")
+    ap.add_argument("--block-rows", type=int, default=0, choices=(0, 64, 128, 256),
+                    help="query rows per workgroup of the bf16 kernel (0: the library's "
+                         "choice from the grid size)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -153,6 +160,10 @@ def main():
     out = torch.empty((wl.B, wl.Hq, wl.Tq, wl.dv), dtype=q.dtype, device=dev)
     mass = torch.empty((wl.B, wl.Hq, wl.Tq), dtype=torch.float32, device=dev)
     mx = torch.empty_like(mass)
+    sets = [(q, k, v, out, mass, mx)]
+    if args.rotate_mib:
+        n_sets = max(1, -(-(args.rotate_mib << 20) // int(alg_bytes(wl))))
+        sets += [tuple(t.clone() for t in sets[0]) for _ in range(n_sets - 1)]
     stream = torch.cuda.current_stream(dev)
     ws = {}
     for var in ("yat", "softmax", "stau"):
@@ -160,9 +171,15 @@ def main():
         ws[var] = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
 
     def call(var):
-        return lambda: attn.attn_fwd(q, k, v, var, causal=wl.causal, out=out, mass=mass,
-                                     max_score=mx, workspace=ws[var], stream=stream.cuda_stream,
-                                     **prm)
+        it = [0]
+
+        def run():
+            q_, k_, v_, o_, m_, x_ = sets[it[0] % len(sets)]
+            it[0] += 1
+            attn.attn_fwd(q_, k_, v_, var, causal=wl.causal, out=o_, mass=m_, max_score=x_,
+                          workspace=ws[var], stream=stream.cuda_stream,
+                          block_rows=args.block_rows, **prm)
+        return run
 
     flops = alg_flops(wl)
     primary = args.variant
@@ -175,6 +192,15 @@ def main():
             others[var] = {"ms": m2, "tflops": flops / (m2 * 1e-3) / 1e12,
                            "frac_bf16_peak": flops / (m2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     value = flops / (mean_ms * 1e-3) / 1e12
+    ai = flops / alg_bytes(wl)
+    hbm_bound = ai < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:   # below the ridge point: the HBM roofline bounds the kernel
+        gbs = alg_bytes(wl) / (mean_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4)}
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean_ms, 4),
@@ -184,15 +210,16 @@ def main():
                                f"dk{wl.dk} dv{wl.dv} {wl.dtype} "
                                f"{'causal' if wl.causal else 'non-causal'}",
                    "variant": primary, "global_batch": wl.B, "seq_len": wl.Tq,
+                   "input_sets_rotated": len(sets), "block_rows": args.block_rows,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {**roof,
                      "traffic": recorded_traffic(wl.name, primary),
                      "traffic_unit": "bytes per launch of attn_fwd_bf16 (HBM, counters)",
                      "kernel": f"|k|^2 pre-pass + attn_fwd_bf16 ({primary}); flops = "
                                f"{flops:.4e} per launch ({wl.allowed_pairs} allowed pairs x "
                                f"2(dk+dv))",
-                     "median_ms": round(med_ms, 4)},
+                     "median_ms": round(med_ms, 4),
+                     "arithmetic_intensity_flop_per_byte": round(ai, 1)},
         "alg_bytes_gbs": round(alg_bytes(wl) / (mean_ms * 1e-3) / 1e9, 1),
         "wall_s_timed_region": round(wall, 3),
     }

@@ -63,9 +63,10 @@ enum {
   ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,       /* a size is negative or zero where it may not be,
                                 Hq % Hkv != 0, or causal with T_q != T_k */
-  ATTN_ERR_UNSUPPORTED = -3, /* dtype, variant or head size not built; a base
-                                pointer or stride breaks the 16-byte alignment
-                                rule; a per-head offset exceeds 2^31 elements */
+  ATTN_ERR_UNSUPPORTED = -3, /* dtype, variant, head size or block_rows not
+                                built; a base pointer or stride breaks the
+                                16-byte alignment rule; a per-head offset
+                                exceeds 2^31 elements */
   ATTN_ERR_PARAM = -4,       /* a per-head parameter the variant needs is NULL */
   ATTN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
   ATTN_ERR_HIP = -6          /* the HIP runtime failed (no device, launch
@@ -83,7 +84,12 @@ enum {
 typedef struct {
   int64_t B, Hq, Hkv, Tq, Tk, dk, dv;
   int32_t dtype; /* attn_dtype */
-  int32_t reserved;
+  /* Query rows per workgroup of the bf16 path: 0 lets the library choose
+   * from the grid size (256-row workgroups when there are enough to fill
+   * the device, else 128 or 64); 64, 128 or 256 force that kernel.  Every
+   * choice computes the same map; results may differ in the last bits only
+   * through the order of the softmax rescale.  The fp32 path takes 0 only. */
+  int32_t block_rows;
   int64_t q_stride[3];
   int64_t k_stride[3];
   int64_t v_stride[3];

@@ -34,7 +34,7 @@ EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_statu
 class AttnDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
                 ("Tq", ctypes.c_int64), ("Tk", ctypes.c_int64), ("dk", ctypes.c_int64),
-                ("dv", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dv", ctypes.c_int64), ("dtype", ctypes.c_int32), ("block_rows", ctypes.c_int32),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
 
@@ -85,8 +85,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def make_desc(q, k, v, out=None) -> AttnDesc:
-    """Descriptor from 4-D tensors (strides in elements, last axis contiguous)."""
+def make_desc(q, k, v, out=None, block_rows=0) -> AttnDesc:
+    """Descriptor from 4-D tensors (strides in elements, last axis contiguous).
+    ``block_rows`` 0 lets the library pick the bf16 kernel; 64/128/256 force one."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t is None:
             continue
@@ -101,6 +102,7 @@ def make_desc(q, k, v, out=None) -> AttnDesc:
     d = AttnDesc()
     d.B, d.Hq, d.Hkv, d.Tq, d.Tk, d.dk, d.dv = B, Hq, Hkv, Tq, Tk, dk, dv
     d.dtype = _dtype_code(q)
+    d.block_rows = int(block_rows)
     for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
         if t is not None:
             getattr(d, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
@@ -117,7 +119,7 @@ def _ptr(t):
 
 
 def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False, out=None,
-             mass=None, max_score=None, workspace=None, stream=None):
+             mass=None, max_score=None, workspace=None, stream=None, block_rows=0):
     """Enqueue the fused forward; returns (out, mass, max_score).
 
     Outputs that are not given are allocated (out like q with d_v columns;
@@ -138,7 +140,7 @@ def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=Fa
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
                               or t.numel() != B * Hq * Tq):
             raise ValueError(f"{name} must be a contiguous float32 tensor of B*Hq*Tq elements")
-    desc = make_desc(q, k, v, out)
+    desc = make_desc(q, k, v, out, block_rows)
     need = int(lib.attn_fwd_workspace_bytes(ctypes.byref(desc), variant))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

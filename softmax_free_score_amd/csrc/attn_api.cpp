@@ -71,6 +71,11 @@ int validate(const attn_desc* d, const void* q, const void* k, const void* v, in
     set_error("unknown dtype");
     return ATTN_ERR_UNSUPPORTED;
   }
+  if (d->block_rows != 0 && (d->dtype != ATTN_BF16 || (d->block_rows != 64 &&
+                             d->block_rows != 128 && d->block_rows != 256))) {
+    set_error("block_rows must be 0, or 64, 128 or 256 with bf16 storage");
+    return ATTN_ERR_UNSUPPORTED;
+  }
   if (!head_dim_ok(d->dk) || !head_dim_ok(d->dv)) {
     set_error("dk and dv must be 16, 32, 64 or 128");
     return ATTN_ERR_UNSUPPORTED;
@@ -156,6 +161,7 @@ int attn_fwd(const attn_desc* d, const void* q, const void* k, const void* v, in
   p.Tq = (int)d->Tq; p.Tk = (int)d->Tk; p.dk = (int)d->dk; p.dv = (int)d->dv;
   p.variant = variant;
   p.causal = causal ? 1 : 0;
+  p.block_rows = d->block_rows;
 
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);

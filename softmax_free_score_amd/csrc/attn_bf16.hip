@@ -584,6 +584,352 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   }
 }
 
+// Fused forward for small grids (fewer query tiles than the ping-pong
+// kernel needs to fill and balance the chip): NW waves x 32 query rows per
+// workgroup, several workgroups per CU, one 64- or 32-key tile per iteration
+// with two LDS stages.  Same layouts and score -> weight maps as above.
+template <int VAR, int DK, int DV, int NW, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_small(Problem p) {
+  constexpr int BM = NW * 32;            // query rows per workgroup
+  constexpr int NT = NW * 64;            // threads
+  constexpr int KS = DK / 16;            // k-steps of the score MFMA
+  constexpr int DVP = DV < 32 ? 32 : DV; // value width padded to the MFMA block
+  constexpr int DB = DVP / 32;           // 32-row blocks of O^T
+  constexpr int KB = BN / 32;            // 32-key blocks per tile
+  constexpr int KLD = DK + 8;            // LDS pitch of K rows (bf16), padded
+  constexpr int VLD = BN + 8;            // LDS pitch of V^T rows (bf16), padded
+  constexpr int KCH = DK / 8;            // 16-byte chunks per K row
+  constexpr int K_UNITS = BN * KCH;
+  constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
+  constexpr int V_UNITS = (BN / 4) * (DV / 8);  // 4 keys x 8 values each
+  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  static_assert(BN % 32 == 0 && BN <= 64, "tiles are 32 or 64 keys");
+
+  // Two LDS stages: the tile being computed and the next one being filled.
+  __shared__ __attribute__((aligned(16))) unsigned short sK[2][BN * KLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[2][DVP * VLD];
+  __shared__ __attribute__((aligned(16))) float sNK[2][BN];
+  __shared__ float sNQ[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  // Workgroup -> (query tile, batch, head).  Heads vary fastest; with a causal
+  // mask the longest query tiles are dispatched first.
+  const int n_qt = (p.Tq + BM - 1) / BM;
+  const int nbh = p.B * p.Hq;
+  int qt = blockIdx.x / nbh;
+  const int bh = blockIdx.x - qt * nbh;
+  if (p.causal) qt = n_qt - 1 - qt;
+  const int b = bh / p.Hq, h = bh - b * p.Hq;
+  const int hk = h / (p.Hq / p.Hkv);
+  const int q0 = qt * BM, qw = q0 + 32 * w, my_q = qw + col;
+
+  const unsigned short* qbase =
+      (const unsigned short*)p.q + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[1];
+  const unsigned short* kbase =
+      (const unsigned short*)p.k + (int64_t)b * p.ks[0] + (int64_t)hk * p.ks[1];
+  const unsigned short* vbase =
+      (const unsigned short*)p.v + (int64_t)b * p.vs[0] + (int64_t)hk * p.vs[1];
+  const uint32_t q_bytes = slice_bytes(p.Tq, p.qs[2], DK);
+  const uint32_t k_bytes = slice_bytes(p.Tk, p.ks[2], DK);
+  const uint32_t v_bytes = slice_bytes(p.Tk, p.vs[2], DV);
+  const rsrc_t rq = make_rsrc(qbase, q_bytes);
+  const rsrc_t rk = make_rsrc(kbase, k_bytes);
+  const rsrc_t rv = make_rsrc(vbase, v_bytes);
+  const int kst = (int)p.ks[2], vst = (int)p.vs[2];
+
+  // Per-head scalars (prologue).
+  float bias = 0.f, eps = 0.f, tau = 0.f;
+  if (VAR == kYat) {
+    bias = softplus_precise(p.b_raw[h]);
+    eps = softplus_precise(p.eps_raw[h]);
+  } else if (VAR == kStau) {
+    tau = softplus_precise(p.log_tau[h]) + 1.f;
+  }
+  const float scale = 1.0f / sqrtf((float)DK);
+
+  // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7].
+  bf16x8 qf[KS];
+  {
+    const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
+                                     : q_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
+    __builtin_amdgcn_s_waitcnt(0);  // not outstanding on entry to the main loop
+  }
+  float nq = 0.f;
+  // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
+  // tile never reads past it (entries >= T_k are masked out).
+  const float* nk_slice =
+      VAR == kYat ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+  if (VAR == kYat) {
+    f32x16 g = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
+    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
+  }
+
+  const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  // Staging registers for the next key/value tile.
+  u32x4 kreg[K_PER_T];
+  u32x4 vreg[V_PER_T][4];
+  f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < K_UNITS) {
+        const int row = k0 + u / KCH, c = u % KCH;
+        const uint32_t off = row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes;
+        kreg[i] = ld128(rk, off);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < V_UNITS) {
+        const int g4 = u % (BN / 4), c = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = k0 + 4 * g4 + r;
+          const uint32_t off = row < p.Tk ? (uint32_t)((row * vst + 8 * c) * 2) : v_bytes;
+          vreg[i][r] = ld128(rv, off);
+        }
+      }
+    }
+    if (VAR == kYat && tid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < K_UNITS) {
+        const int j = u / KCH, c = u % KCH;
+        const int row = (j & ~31) | k_lds_row(j & 31);
+        *(u32x4*)&sK[buf][row * KLD + 8 * c] = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < V_UNITS) {
+        const int g4 = u % (BN / 4), c = u / (BN / 4);
+        // 4 keys x 8 values -> 8 value rows of 4 keys each.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
+          const unsigned a2 = vreg[i][2][e], a3 = vreg[i][3][e];
+          u32x2 lo, hi;
+          lo[0] = (a0 & 0xffffu) | (a1 << 16);
+          lo[1] = (a2 & 0xffffu) | (a3 << 16);
+          hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+          hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+          *(u32x2*)&sV[buf][(8 * c + 2 * e) * VLD + 4 * g4] = lo;
+          *(u32x2*)&sV[buf][(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
+        }
+      }
+    }
+    if (VAR == kYat && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x16{};
+  float mass = 0.f;       // Yat, s^tau: sum of weights; softmax: sum exp2(x - mref)
+  float mx = -INFINITY;   // Yat: max kappa; s^tau: max s; softmax: max of x = s*log2e/sqrt(dk)
+  float mref = -INFINITY; // softmax: reference maximum of the exponentials
+  const float c_sm = scale * kLog2e;
+
+  // One tile of BN keys against the wave's 32 queries.
+  auto compute = [&](auto mask_tag, int buf, int k0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const unsigned short* K = sK[buf];
+    const unsigned short* Vt = sV[buf];
+
+    // S^T = K Q^T, the KB accumulation chains interleaved.
+    f32x16 sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *(const u32x4*)&K[(kb * 32 + col) * KLD + 16 * s + 8 * half]);
+        sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+      }
+
+    auto allowed = [&](int kb, int r) {
+      const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+      return !((p.causal && key > my_q) || key >= p.Tk);
+    };
+
+    if (VAR == kSoftmax) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kb][r] * c_sm;
+          if (MASK) x = allowed(kb, r) ? x : -INFINITY;
+          sacc[kb][r] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = pair_max(tmax);
+      mx = fmaxf(mx, tmax);
+      if (tmax > mref + kRescaleSlack) {  // first tile: mref = -inf
+        const float alpha = __builtin_amdgcn_exp2f(mref - tmax);
+        mass *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) o[d] *= alpha;
+        mref = tmax;
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(sacc[kb][r] - mref);
+          sacc[kb][r] = e;
+          mass += e;
+        }
+    } else if (VAR == kYat) {
+      const float* NK = sNK[buf];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        // (read as float vectors: this compiler mis-evaluates a bit_cast of a
+        // single vector element)
+        const f32x4 n0 = *(const f32x4*)&NK[kb * 32 + 8 * half];
+        const f32x4 n1 = *(const f32x4*)&NK[kb * 32 + 8 * half + 4];
+        const f32x4 n2 = *(const f32x4*)&NK[kb * 32 + 16 + 8 * half];
+        const f32x4 n3 = *(const f32x4*)&NK[kb * 32 + 16 + 8 * half + 4];
+        float nk[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nk[e] = n0[e];
+          nk[4 + e] = n1[e];
+          nk[8 + e] = n2[e];
+          nk[12 + e] = n3[e];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sacc[kb][r];
+          const float d2 = fmaf(-2.f, s, nq + nk[r]);
+          const float u = s + bias;
+          float kap = u * u * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
+          if (MASK) kap = allowed(kb, r) ? kap : 0.f;
+          sacc[kb][r] = kap;
+          mass += kap;
+          mx = fmaxf(mx, kap);
+        }
+      }
+    } else {  // s^tau
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sacc[kb][r] * scale;
+          // softplus(s) = max(s, 0) + log1p(e), e = exp(-|s|) in (0, 1].  The
+          // rounding error c of u1 = 1 + e is exact (u1 - 1 - e); log1p(e) =
+          // ln(u1) - c/u1 to first order, and c/u1 = c within a relative e.
+          const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+          const float u1 = 1.f + e;
+          const float c = (u1 - 1.f) - e;
+          const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
+          float u = __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(sp + 1e-6f));
+          float sm = s;
+          if (MASK) {
+            const bool ok = allowed(kb, r);
+            u = ok ? u : 0.f;
+            sm = ok ? s : -INFINITY;
+          }
+          sacc[kb][r] = u;
+          mass += u;
+          mx = fmaxf(mx, sm);
+        }
+    }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 pw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)&Vt[(32 * d + col) * VLD + kb * 32 + 16 * s + 8 * half]);
+          o[d] = mfma32(a, pb, o[d]);
+        }
+      }
+  };
+
+  // Prologue: tile 0 into stage 0, tile 1 into registers.
+  load_tile(0);
+  store_tile(0);
+  if (n_tiles > 1) load_tile(BN);
+  __syncthreads();
+  if (VAR == kYat) nq = sNQ[32 * w + col];
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = t * BN, buf = t & 1;
+    // every key of the tile is in this wave's future: nothing to do
+    if (!(p.causal && k0 > qw + 31)) {
+      const bool need_mask = (p.causal && k0 + BN - 1 > qw) || (k0 + BN > p.Tk);
+      if (need_mask) compute(std::true_type{}, buf, k0);
+      else compute(std::false_type{}, buf, k0);
+    }
+    if (t + 1 < n_tiles) {
+      // Stage t+1 was last read in iteration t-1, which every wave finished
+      // before the barrier that ended it.
+      store_tile(buf ^ 1);
+      if (t + 2 < n_tiles) load_tile(k0 + 2 * BN);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: combine the two lanes that share a query, normalise, store.
+  float mass_all = pair_sum(mass);
+  const float mx_all = pair_max(mx);
+  if (VAR == kSoftmax) mass_all *= __builtin_amdgcn_exp2f(mref - mx_all);  // relative to the max
+  float inv;
+  if (VAR == kYat) inv = 1.f / (mass_all + 1e-9f);
+  else if (VAR == kSoftmax) inv = 1.f / mass_all;
+  else inv = mass_all > 0.f ? 1.f / mass_all : 0.f;
+  // softmax: O holds sum exp2(x - mref) v; mass_all is relative to mx_all
+  const float oscale = VAR == kSoftmax ? inv * __builtin_amdgcn_exp2f(mref - mx_all) : inv;
+  if (my_q < p.Tq) {
+    unsigned short* orow = (unsigned short*)p.out + (int64_t)b * p.os[0] +
+                           (int64_t)h * p.os[1] + (int64_t)my_q * p.os[2];
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dv0 = 32 * d + 8 * g4 + 4 * half;
+        if (dv0 < DV) {
+          u32x2 st;
+          st[0] = pack_bf16(o[d][4 * g4] * oscale, o[d][4 * g4 + 1] * oscale);
+          st[1] = pack_bf16(o[d][4 * g4 + 2] * oscale, o[d][4 * g4 + 3] * oscale);
+          *(u32x2*)&orow[dv0] = st;
+        }
+      }
+    if (half == 0) {
+      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
+      if (p.mass) p.mass[ri] = mass_all;
+      if (p.max_score) p.max_score[ri] = VAR == kSoftmax ? mx_all * kLn2 : mx_all;
+    }
+  }
+}
+
 // Keys per tile.
 #ifndef SFS_BN
 #define SFS_BN 64
@@ -593,15 +939,30 @@ template <int VAR, int DV>
 hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   constexpr int DK = SFS_DK;
   constexpr int BN = SFS_BN;
-  constexpr int BM = 256;  // query rows per workgroup (8 waves)
   if (VAR == kYat) {
     const dim3 grid((p.Tk + 127) / 128, p.Hkv, p.B);
     hipLaunchKernelGGL(row_norms_bf16<DK>, grid, dim3(256), 0, stream,
                        (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk, p.nk);
   }
-  const int n_qt = (p.Tq + BM - 1) / BM;
-  const unsigned n_wg = (unsigned)n_qt * (unsigned)p.B * (unsigned)p.Hq;
-  hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(n_wg), dim3(512), 0, stream, p);
+  // 256-row ping-pong workgroups when there are enough of them to fill the
+  // chip (and, with a causal mask, to balance tiles of unequal length);
+  // otherwise 128- or 64-row workgroups, several per CU.
+  const unsigned bh = (unsigned)p.B * (unsigned)p.Hq;
+  const unsigned n256 = (unsigned)((p.Tq + 255) / 256) * bh;
+  const unsigned n128 = (unsigned)((p.Tq + 127) / 128) * bh;
+  const unsigned n64 = (unsigned)((p.Tq + 63) / 64) * bh;
+  const unsigned cus = 256;
+  int rows = p.block_rows;
+  if (rows == 0) rows = n256 >= (p.causal ? 4 * cus : cus) ? 256 : n128 >= cus ? 128 : 64;
+  if (rows == 256) {
+    hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(n256), dim3(512), 0, stream, p);
+  } else if (rows == 128) {
+    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64>), dim3(n128), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32>), dim3(n64), dim3(128), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 

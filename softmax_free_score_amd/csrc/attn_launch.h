@@ -31,6 +31,7 @@ struct Problem {
   int B, Hq, Hkv, Tq, Tk, dk, dv;
   int variant;
   int causal;
+  int block_rows;  // 0: choose by grid size; 64, 128, 256: force that kernel
 };
 
 // Fused forward for fp32 storage (vector-ALU path).

@@ -88,6 +88,21 @@ def test_unsupported():
     assert call(d) == ERR_UNSUP
 
 
+@pytest.mark.parametrize("rows,dtype,status", [(32, attn.ATTN_BF16, ERR_UNSUP),
+                                               (512, attn.ATTN_BF16, ERR_UNSUP),
+                                               (-64, attn.ATTN_BF16, ERR_UNSUP),
+                                               (64, attn.ATTN_F32, ERR_UNSUP),
+                                               (64, attn.ATTN_BF16, ERR_HIP),
+                                               (128, attn.ATTN_BF16, ERR_HIP),
+                                               (256, attn.ATTN_BF16, ERR_HIP)])
+def test_block_rows(rows, dtype, status):
+    # valid choices pass validation and then fail on the missing device
+    d = desc(dtype=dtype)
+    assert d.block_rows == 0                          # attn_desc_init: library's choice
+    d.block_rows = rows
+    assert call(d) == status
+
+
 def test_missing_per_head_parameters():
     assert call(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
     assert call(desc(), variant=attn.ATTN_YAT, e=0) == ERR_PARAM

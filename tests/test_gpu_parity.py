@@ -21,13 +21,19 @@ def v_max(inp):
     return float(np.abs(inp.v).max())
 
 
-def full_check(inp, variant, causal, label):
+# bf16 kernels by query rows per workgroup (0: the library's own choice)
+BLOCK_ROWS = (0, 64, 128, 256)
+
+
+def full_check(inp, variant, causal, label, block_rows=(0,)):
     say(f"[gpu] {label} {variant} causal={causal} shape B{inp.wl.B} Hq{inp.wl.Hq} "
         f"Hkv{inp.wl.Hkv} Tq{inp.wl.Tq} Tk{inp.wl.Tk} dk{inp.wl.dk} dv{inp.wl.dv} {inp.wl.dtype}")
     q, k, v, prm = to_device(inp)
-    got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal)]
     ref = oracle_full(inp, variant, causal)
-    return check(inp.wl.dtype, got, ref, v_max(inp), f"{label}/{variant}", v_rms=v_rms(inp))
+    for rows in block_rows:
+        got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal, block_rows=rows)]
+        check(inp.wl.dtype, got, ref, v_max(inp), f"{label}/{variant}/rows{rows}",
+              v_rms=v_rms(inp))
 
 
 # ---------------------------------------------------------------- small sizes
@@ -47,7 +53,7 @@ def test_gpt_small_full(variant):
 def test_gpt_small_tied_yat():
     # k := q puts the Yat peak (|q|^2 + b)^2 / eps on the diagonal
     inp = make_inputs(WORKLOADS["gpt_small"], tied=True)
-    full_check(inp, "yat", True, "gpt_small_tied")
+    full_check(inp, "yat", True, "gpt_small_tied", BLOCK_ROWS)
 
 
 MEDIUM = [
@@ -68,7 +74,7 @@ MEDIUM = [
 def test_medium_shapes_bf16(variant, shape):
     B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
     inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=7, qk_std=1.5)
-    full_check(inp, variant, causal, "medium")
+    full_check(inp, variant, causal, "medium", BLOCK_ROWS)
 
 
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
@@ -84,7 +90,7 @@ def test_medium_shapes_fp32(variant, shape):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_tied_medium_yat(dtype):
     inp = make_custom(1, 3, 3, 300, 300, 128, 128, dtype, True, seed=9, qk_std=2.0, tied=True)
-    full_check(inp, "yat", True, "tied_medium")
+    full_check(inp, "yat", True, "tied_medium", BLOCK_ROWS if dtype == "bf16" else (0,))
 
 
 # --------------------------------------------------------------- edge cases
@@ -98,7 +104,8 @@ def test_degenerate_sizes(variant, shape):
     B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
     for dtype in ("bf16", "f32"):
         inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, dtype, causal, seed=10)
-        full_check(inp, variant, causal, f"degenerate_{dtype}")
+        full_check(inp, variant, causal, f"degenerate_{dtype}",
+                   BLOCK_ROWS if dtype == "bf16" else (0,))
 
 
 def test_empty_batch_is_a_no_op():
@@ -139,29 +146,31 @@ def test_strided_layout_and_null_statistics(variant):
 
 # ------------------------------------------------------------- invariances
 
+@pytest.mark.parametrize("rows", BLOCK_ROWS[1:])
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
-def test_causality_and_determinism(variant):
+def test_causality_and_determinism(variant, rows):
     inp = make_custom(1, 2, 2, 384, 384, 128, 128, "bf16", True, seed=12)
     q, k, v, prm = to_device(inp)
-    a = run_gpu(q, k, v, prm, variant, True)
-    b = run_gpu(q, k, v, prm, variant, True)
+    a = run_gpu(q, k, v, prm, variant, True, block_rows=rows)
+    b = run_gpu(q, k, v, prm, variant, True, block_rows=rows)
     for x, y in zip(a, b):
         assert torch.equal(x, y), "two identical calls differ"
     k2, v2 = k.clone(), v.clone()
     k2[:, :, 200:] = -k2[:, :, 200:]
     v2[:, :, 200:] = 3.0
-    c = run_gpu(q, k2, v2, prm, variant, True)
+    c = run_gpu(q, k2, v2, prm, variant, True, block_rows=rows)
     for x, y in zip(a, c):
         assert torch.equal(x[:, :, :200], y[:, :, :200]), "a row saw a future key"
 
 
+@pytest.mark.parametrize("rows", BLOCK_ROWS[1:])
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
-def test_gqa_equals_repeated_kv(variant):
+def test_gqa_equals_repeated_kv(variant, rows):
     inp = make_custom(2, 8, 2, 200, 200, 64, 64, "bf16", True, seed=13)
     q, k, v, prm = to_device(inp)
-    a = run_gpu(q, k, v, prm, variant, True)
+    a = run_gpu(q, k, v, prm, variant, True, block_rows=rows)
     b = run_gpu(q, k.repeat_interleave(4, dim=1).contiguous(),
-                v.repeat_interleave(4, dim=1).contiguous(), prm, variant, True)
+                v.repeat_interleave(4, dim=1).contiguous(), prm, variant, True, block_rows=rows)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
