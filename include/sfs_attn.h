@@ -135,6 +135,34 @@ int attn_fwd(const attn_desc* desc, const void* q, const void* k, const void* v,
              void* out, float* mass, float* max_score, void* workspace,
              size_t workspace_bytes, void* stream);
 
+/* Yat kernel-family options.
+ *
+ * "The Kernel Between the Roles", section "The run": raising the power of the
+ * numerator, (q.k)^(2m), is named as the dial that sharpens the kernel's peak
+ * while keeping its structure; the same section measures the b = 0 ablation
+ * (the non-universal special case, where an orthogonal query-key pair scores
+ * exactly zero).  Here both are options of the Yat map:
+ *   kappa = (q.k + b)^(2 power) / (max(|q|^2 + |k|^2 - 2 q.k, 0) + eps),
+ * with b = softplus(b_raw[h]), or b = 0 exactly when bias_free is nonzero
+ * (b_raw is then not read and may be NULL).  power = 1, bias_free = 0 is the
+ * standard kernel that attn_fwd(ATTN_YAT) computes.  Domain: kappa and the
+ * row mass must stay finite in fp32, i.e. |q.k + b|^(2 power) / eps summed
+ * over a row below ~3e38. */
+#define ATTN_YAT_MAX_POWER 8
+typedef struct {
+  int32_t power;     /* m in 1 .. ATTN_YAT_MAX_POWER */
+  int32_t bias_free; /* nonzero: b = 0 exactly */
+} attn_yat_opts;
+
+/* The Yat forward with kernel-family options.  Arguments, layouts, workspace
+ * (attn_fwd_workspace_bytes(desc, ATTN_YAT)), ownership and errors are those
+ * of attn_fwd with variant ATTN_YAT; opts == NULL means {1, 0}.  A power
+ * outside 1 .. ATTN_YAT_MAX_POWER returns ATTN_ERR_UNSUPPORTED. */
+int attn_fwd_yat(const attn_desc* desc, const void* q, const void* k, const void* v,
+                 const float* b_raw, const float* eps_raw, const attn_yat_opts* opts,
+                 int causal, void* out, float* mass, float* max_score, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

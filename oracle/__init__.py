@@ -77,6 +77,10 @@ def _load():
                                         i64, i64, d, d, d, d, d, d,
                                         ctypes.POINTER(i64), i64, d, d, d]
         lib.oracle_attn_fwd.restype = ctypes.c_int
+        lib.oracle_attn_fwd_yat.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
+                                            d, d, d, d, d, ctypes.c_int, ctypes.c_int,
+                                            ctypes.POINTER(i64), i64, d, d, d]
+        lib.oracle_attn_fwd_yat.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -97,7 +101,7 @@ def _as_f64(a):
 
 
 def attn_fwd_c(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False,
-               rows=None):
+               rows=None, yat_power=1, yat_bias_free=False):
     """C oracle.  q [B,Hq,Tq,dk], k [B,Hkv,Tk,dk], v [B,Hkv,Tk,dv] (any float
     dtype; upcast exactly to fp64).  ``rows`` optionally lists flat row ids
     (b*Hq + h)*Tq + i to evaluate.  Returns (out, mass, max_score); with
@@ -117,11 +121,16 @@ def attn_fwd_c(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=
     out = np.empty((n, dv), np.float64)
     mass = np.empty(n, np.float64)
     mx = np.empty(n, np.float64)
-    rc = _load().oracle_attn_fwd(
-        int(variant), int(bool(causal)), B, Hq, Hkv, Tq, Tk, dk, dv, _dptr(q), _dptr(k),
-        _dptr(v), *[_dptr(p) for p in params],
-        None if rows_arr is None else rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-        n, _dptr(out), _dptr(mass), _dptr(mx))
+    rows_p = None if rows_arr is None else rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    if variant == YAT and (yat_power != 1 or yat_bias_free):
+        rc = _load().oracle_attn_fwd_yat(
+            int(bool(causal)), B, Hq, Hkv, Tq, Tk, dk, dv, _dptr(q), _dptr(k), _dptr(v),
+            _dptr(params[0]), _dptr(params[1]), int(yat_power), int(bool(yat_bias_free)),
+            rows_p, n, _dptr(out), _dptr(mass), _dptr(mx))
+    else:
+        rc = _load().oracle_attn_fwd(
+            int(variant), int(bool(causal)), B, Hq, Hkv, Tq, Tk, dk, dv, _dptr(q), _dptr(k),
+            _dptr(v), *[_dptr(p) for p in params], rows_p, n, _dptr(out), _dptr(mass), _dptr(mx))
     if rc != 0:
         raise ValueError(f"oracle_attn_fwd rejected its arguments (code {rc})")
     if rows is None:
@@ -135,8 +144,12 @@ def softplus(x):
     return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
 
 
-def attn_fwd_np(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False):
-    """numpy fp64 oracle; same contract as ``attn_fwd_c`` without ``rows``."""
+def attn_fwd_np(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False,
+                yat_power=1, yat_bias_free=False):
+    """numpy fp64 oracle; same contract as ``attn_fwd_c`` without ``rows``.
+
+    Yat options ("The Kernel Between the Roles", "The run"): numerator
+    (q.k + b)^(2 yat_power); b = 0 exactly when ``yat_bias_free``."""
     variant = VARIANTS.get(variant, variant)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     B, Hq, Tq, dk = q.shape
@@ -152,11 +165,11 @@ def attn_fwd_np(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal
     if causal:
         allowed = np.tril(allowed)
     if variant == YAT:
-        bias = softplus(b_raw)[None, :, None, None]
+        bias = 0.0 if yat_bias_free else softplus(b_raw)[None, :, None, None]
         eps = softplus(eps_raw)[None, :, None, None]
         d2 = (np.sum(q * q, -1, keepdims=True) + np.swapaxes(np.sum(kh * kh, -1, keepdims=True), -1, -2)
               - 2.0 * dots)
-        kappa = (dots + bias) ** 2 / (np.maximum(d2, 0.0) + eps)
+        kappa = ((dots + bias) ** 2) ** int(yat_power) / (np.maximum(d2, 0.0) + eps)
         kappa = np.where(allowed, kappa, 0.0)
         mass = kappa.sum(-1)
         w = kappa / (mass[..., None] + 1e-9)

@@ -17,6 +17,10 @@
  *   [P3] "NNX Scaled Dot-Product Attention", sections "Shapes and the three
  *        steps", "Mask before softmax" and the displayed equation
  *        A = softmax(QK^T / sqrt(d_k) + M), O = AV.
+ *   [P2'] "The Kernel Between the Roles", section "The run": the numerator
+ *        power (q.k)^(2m) as the dial that sharpens the kernel's peak, and the
+ *        b = 0 ablation.  Options of the Yat branch here:
+ *        kappa = (dots + b)^(2m) / (max(d2, 0) + eps), b = 0 when bias-free.
  *   [P5] "s^tau" forum post, section with the core formula:
  *        a_i = phi(s_i)^tau / sum_j phi(s_j)^tau, phi(s) = softplus(s) + eps,
  *        tau = softplus(log_tau) + 1.
@@ -60,8 +64,9 @@ static double dot(const double* a, const double* b, int64_t n) {
 static void one_row(int variant, int causal, int64_t Hq, int64_t Hkv, int64_t Tq,
                     int64_t Tk, int64_t dk, int64_t dv, const double* q,
                     const double* k, const double* v, const double* b_raw,
-                    const double* eps_raw, const double* log_tau, int64_t row,
-                    double* score, double* out, double* mass, double* max_score) {
+                    const double* eps_raw, const double* log_tau, int yat_power,
+                    int yat_bias_free, int64_t row, double* score, double* out,
+                    double* mass, double* max_score) {
   const int64_t i = row % Tq;
   const int64_t bh = row / Tq;
   const int64_t h = bh % Hq;
@@ -77,7 +82,7 @@ static void one_row(int variant, int causal, int64_t Hq, int64_t Hkv, int64_t Tq
     /* [P1]: dots, d2 = |q|^2 + |k|^2 - 2 dots, b = softplus(b_raw),
      * eps = softplus(eps_raw), kappa = (dots + b)^2 / (max(d2, 0) + eps),
      * kappa = 0 where masked, mass = sum kappa, w = kappa / (mass + 1e-9). */
-    const double bias = softplus(b_raw[h]);
+    const double bias = yat_bias_free ? 0.0 : softplus(b_raw[h]);
     const double eps = softplus(eps_raw[h]);
     const double nq = dot(qi, qi, dk);
     for (int64_t j = 0; j < Tk; ++j) {
@@ -85,7 +90,10 @@ static void one_row(int variant, int causal, int64_t Hq, int64_t Hkv, int64_t Tq
       const double* kj = kb + j * dk;
       const double s = dot(qi, kj, dk);
       const double d2 = nq + dot(kj, kj, dk) - 2.0 * s;
-      const double kappa = (s + bias) * (s + bias) / (fmax(d2, 0.0) + eps);
+      /* [P2']: numerator (s + b)^(2m), m = yat_power (m = 1: [P1]) */
+      double num = 1.0;
+      for (int e = 0; e < yat_power; ++e) num *= (s + bias) * (s + bias);
+      const double kappa = num / (fmax(d2, 0.0) + eps);
       score[j] = kappa;
       total += kappa;
       if (kappa > m) m = kappa;
@@ -130,15 +138,16 @@ static void one_row(int variant, int causal, int64_t Hq, int64_t Hkv, int64_t Tq
 }
 
 /* Returns 0 on success, -1 on a bad argument, -2 when scratch can't be had. */
-int oracle_attn_fwd(int variant, int causal, int64_t B, int64_t Hq, int64_t Hkv,
-                    int64_t Tq, int64_t Tk, int64_t dk, int64_t dv, const double* q,
-                    const double* k, const double* v, const double* b_raw,
-                    const double* eps_raw, const double* log_tau, const int64_t* rows,
-                    int64_t n_rows, double* out, double* mass, double* max_score) {
+static int attn_rows(int variant, int causal, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq,
+                     int64_t Tk, int64_t dk, int64_t dv, const double* q, const double* k,
+                     const double* v, const double* b_raw, const double* eps_raw,
+                     const double* log_tau, int yat_power, int yat_bias_free,
+                     const int64_t* rows, int64_t n_rows, double* out, double* mass,
+                     double* max_score) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Tq < 0 || Tk <= 0 || dk <= 0 ||
-      dv <= 0 || (causal && Tq != Tk) || variant < 0 || variant > 2)
+      dv <= 0 || (causal && Tq != Tk) || variant < 0 || variant > 2 || yat_power < 1)
     return -1;
-  if (variant == ORACLE_YAT && (!b_raw || !eps_raw)) return -1;
+  if (variant == ORACLE_YAT && ((!b_raw && !yat_bias_free) || !eps_raw)) return -1;
   if (variant == ORACLE_STAU && !log_tau) return -1;
   const int64_t total_rows = B * Hq * Tq;
   if (!rows) n_rows = total_rows;
@@ -157,11 +166,31 @@ int oracle_attn_fwd(int variant, int causal, int64_t B, int64_t Hq, int64_t Hkv,
       }
       const int64_t row = rows ? rows[r] : r;
       one_row(variant, causal, Hq, Hkv, Tq, Tk, dk, dv, q, k, v, b_raw, eps_raw, log_tau,
-              row, score, out + r * dv, mass + r, max_score + r);
+              yat_power, yat_bias_free, row, score, out + r * dv, mass + r, max_score + r);
     }
     free(score);
   }
   return failed ? -2 : 0;
+}
+
+int oracle_attn_fwd(int variant, int causal, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t Tq, int64_t Tk, int64_t dk, int64_t dv, const double* q,
+                    const double* k, const double* v, const double* b_raw,
+                    const double* eps_raw, const double* log_tau, const int64_t* rows,
+                    int64_t n_rows, double* out, double* mass, double* max_score) {
+  return attn_rows(variant, causal, B, Hq, Hkv, Tq, Tk, dk, dv, q, k, v, b_raw, eps_raw,
+                   log_tau, 1, 0, rows, n_rows, out, mass, max_score);
+}
+
+/* The Yat branch with the kernel-family options of [P2']: numerator power
+ * m = yat_power >= 1, and b = 0 exactly when yat_bias_free (b_raw unused). */
+int oracle_attn_fwd_yat(int causal, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq,
+                        int64_t Tk, int64_t dk, int64_t dv, const double* q, const double* k,
+                        const double* v, const double* b_raw, const double* eps_raw,
+                        int yat_power, int yat_bias_free, const int64_t* rows,
+                        int64_t n_rows, double* out, double* mass, double* max_score) {
+  return attn_rows(ORACLE_YAT, causal, B, Hq, Hkv, Tq, Tk, dk, dv, q, k, v, b_raw, eps_raw,
+                   NULL, yat_power, yat_bias_free, rows, n_rows, out, mass, max_score);
 }
 
 /* Threads the parallel loop above runs on (1 without OpenMP). */

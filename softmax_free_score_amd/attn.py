@@ -27,8 +27,9 @@ ATTN_F32, ATTN_BF16 = 0, 1
 VARIANTS = {"softmax": ATTN_SOFTMAX, "yat": ATTN_YAT, "stau": ATTN_STAU}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
           -4: "ATTN_ERR_PARAM", -5: "ATTN_ERR_WORKSPACE", -6: "ATTN_ERR_HIP"}
-EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_status_string",
-           "attn_last_error")
+EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_yat",
+           "attn_status_string", "attn_last_error")
+ATTN_YAT_MAX_POWER = 8
 
 
 class AttnDesc(ctypes.Structure):
@@ -37,6 +38,10 @@ class AttnDesc(ctypes.Structure):
                 ("dv", ctypes.c_int64), ("dtype", ctypes.c_int32), ("block_rows", ctypes.c_int32),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
                 ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+
+
+class AttnYatOpts(ctypes.Structure):
+    _fields_ = [("power", ctypes.c_int32), ("bias_free", ctypes.c_int32)]
 
 
 class AttnError(RuntimeError):
@@ -69,6 +74,10 @@ def load_library():
         lib.attn_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                  ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd_yat.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp,
+                                     ctypes.POINTER(AttnYatOpts), ctypes.c_int, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+        lib.attn_fwd_yat.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -118,16 +127,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False, out=None,
-             mass=None, max_score=None, workspace=None, stream=None, block_rows=0):
-    """Enqueue the fused forward; returns (out, mass, max_score).
-
-    Outputs that are not given are allocated (out like q with d_v columns;
-    mass and max_score float32 [B,Hq,Tq]); a workspace of the required size is
-    allocated when not given.  ``stream`` defaults to torch's current stream
-    on q's device.  Raises AttnError with the library's status on failure."""
+def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_rows):
     lib = load_library()
-    variant = VARIANTS.get(variant, variant)
     B, Hq, Tq, _ = q.shape
     dv = v.shape[3]
     if out is None:
@@ -147,10 +148,41 @@ def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=Fa
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    return lib, desc, out, mass, max_score, workspace, ws_bytes, stream
+
+
+def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False, out=None,
+             mass=None, max_score=None, workspace=None, stream=None, block_rows=0):
+    """Enqueue the fused forward; returns (out, mass, max_score).
+
+    Outputs that are not given are allocated (out like q with d_v columns;
+    mass and max_score float32 [B,Hq,Tq]); a workspace of the required size is
+    allocated when not given.  ``stream`` defaults to torch's current stream
+    on q's device.  Raises AttnError with the library's status on failure."""
+    variant = VARIANTS.get(variant, variant)
+    lib, desc, out, mass, max_score, workspace, ws_bytes, stream = _prepare(
+        q, k, v, variant, out, mass, max_score, workspace, stream, block_rows)
     st = lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), variant, _ptr(b_raw),
                       _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(out), _ptr(mass),
                       _ptr(max_score), _ptr(workspace), ws_bytes,
                       ctypes.c_void_p(stream) if stream else None)
+    if st != 0:
+        raise AttnError(st, lib.attn_last_error().decode())
+    return out, mass, max_score
+
+
+def attn_fwd_yat(q, k, v, b_raw=None, eps_raw=None, power=1, bias_free=False, causal=False,
+                 out=None, mass=None, max_score=None, workspace=None, stream=None, block_rows=0):
+    """The Yat forward with kernel-family options: numerator (q.k + b)^(2 power),
+    and b = 0 exactly when ``bias_free`` (b_raw then unused).  Otherwise as
+    ``attn_fwd(..., "yat", ...)``."""
+    lib, desc, out, mass, max_score, workspace, ws_bytes, stream = _prepare(
+        q, k, v, ATTN_YAT, out, mass, max_score, workspace, stream, block_rows)
+    opts = AttnYatOpts(int(power), int(bool(bias_free)))
+    st = lib.attn_fwd_yat(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(b_raw),
+                          _ptr(eps_raw), ctypes.byref(opts), int(bool(causal)), _ptr(out),
+                          _ptr(mass), _ptr(max_score), _ptr(workspace), ws_bytes,
+                          ctypes.c_void_p(stream) if stream else None)
     if st != 0:
         raise AttnError(st, lib.attn_last_error().decode())
     return out, mass, max_score
@@ -165,3 +197,16 @@ def call_raw(desc: AttnDesc, q, k, v, variant, b_raw, eps_raw, log_tau, causal, 
     return int(lib.attn_fwd(dp, p(q), p(k), p(v), int(variant), p(b_raw),
                             p(eps_raw), p(log_tau), int(causal), p(out), p(mass), p(max_score),
                             p(workspace), int(workspace_bytes), p(stream)))
+
+
+def call_raw_yat(desc: AttnDesc, q, k, v, b_raw, eps_raw, opts, causal, out, mass, max_score,
+                 workspace, workspace_bytes, stream) -> int:
+    """attn_fwd_yat with raw integer pointers (0 = NULL) and an AttnYatOpts or
+    None; returns the status."""
+    lib = load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    dp = ctypes.byref(desc) if desc is not None else None
+    op = ctypes.byref(opts) if opts is not None else None
+    return int(lib.attn_fwd_yat(dp, p(q), p(k), p(v), p(b_raw), p(eps_raw), op, int(causal),
+                                p(out), p(mass), p(max_score), p(workspace),
+                                int(workspace_bytes), p(stream)))

@@ -39,7 +39,7 @@ bool strides_ok(const int64_t s[3], int64_t rows, int64_t d, int64_t elem) {
 int validate(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
              const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
              const void* out, const float* mass, const float* max_score, const void* ws,
-             size_t ws_bytes, bool* empty) {
+             size_t ws_bytes, bool yat_bias_free, bool* empty) {
   *empty = false;
   if (!d) {
     set_error("desc is NULL");
@@ -88,8 +88,8 @@ int validate(const attn_desc* d, const void* q, const void* k, const void* v, in
     set_error("q, k, v and out are required");
     return ATTN_ERR_NULL;
   }
-  if (variant == ATTN_YAT && (!b_raw || !eps_raw)) {
-    set_error("the Yat map needs b_raw and eps_raw");
+  if (variant == ATTN_YAT && ((!b_raw && !yat_bias_free) || !eps_raw)) {
+    set_error("the Yat map needs eps_raw, and b_raw unless it is bias-free");
     return ATTN_ERR_PARAM;
   }
   if (variant == ATTN_STAU && !log_tau) {
@@ -139,19 +139,25 @@ size_t attn_fwd_workspace_bytes(const attn_desc* d, int variant) {
   return (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * sizeof(float);
 }
 
-int attn_fwd(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
-             const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
-             void* out, float* mass, float* max_score, void* workspace, size_t workspace_bytes,
-             void* stream) {
+}  // extern "C"
+
+namespace {
+
+int run(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
+        const float* b_raw, const float* eps_raw, const float* log_tau, int yat_power,
+        int yat_bias_free, int causal, void* out, float* mass, float* max_score,
+        void* workspace, size_t workspace_bytes, void* stream) {
   bool empty = false;
   const int st = validate(d, q, k, v, variant, b_raw, eps_raw, log_tau, causal, out, mass,
-                          max_score, workspace, workspace_bytes, &empty);
+                          max_score, workspace, workspace_bytes, yat_bias_free != 0, &empty);
   if (st != ATTN_OK || empty) return st;
 
   sfs::Problem p{};
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.mass = mass; p.max_score = max_score;
   p.b_raw = b_raw; p.eps_raw = eps_raw; p.log_tau = log_tau;
+  // bias-free Yat does not read b_raw; keep the pointer valid all the same
+  if (variant == ATTN_YAT && yat_bias_free && !b_raw) p.b_raw = eps_raw;
   p.nk = static_cast<float*>(workspace);
   for (int i = 0; i < 3; ++i) {
     p.qs[i] = d->q_stride[i]; p.ks[i] = d->k_stride[i];
@@ -162,6 +168,8 @@ int attn_fwd(const attn_desc* d, const void* q, const void* k, const void* v, in
   p.variant = variant;
   p.causal = causal ? 1 : 0;
   p.block_rows = d->block_rows;
+  p.yat_power = yat_power;
+  p.yat_bias_free = yat_bias_free ? 1 : 0;
 
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -187,12 +195,39 @@ int attn_fwd(const attn_desc* d, const void* q, const void* k, const void* v, in
   return ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
+             const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
+             void* out, float* mass, float* max_score, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return run(d, q, k, v, variant, b_raw, eps_raw, log_tau, 1, 0, causal, out, mass, max_score,
+             workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_yat(const attn_desc* d, const void* q, const void* k, const void* v,
+                 const float* b_raw, const float* eps_raw, const attn_yat_opts* opts, int causal,
+                 void* out, float* mass, float* max_score, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const int power = opts ? opts->power : 1;
+  const int bias_free = opts ? opts->bias_free : 0;
+  if (power < 1 || power > ATTN_YAT_MAX_POWER) {
+    set_error("Yat numerator power must be 1 .. ATTN_YAT_MAX_POWER");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  return run(d, q, k, v, ATTN_YAT, b_raw, eps_raw, nullptr, power, bias_free, causal, out, mass,
+             max_score, workspace, workspace_bytes, stream);
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, variant, head size, alignment or size";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported dtype, variant, head size, option, alignment or size";
     case ATTN_ERR_PARAM: return "a per-head parameter the variant needs is NULL";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP runtime error";

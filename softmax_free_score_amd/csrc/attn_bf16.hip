@@ -227,8 +227,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 
   // Per-head scalars (prologue).
   float bias = 0.f, eps = 0.f, tau = 0.f;
-  if (VAR == kYat) {
-    bias = softplus_precise(p.b_raw[h]);
+  if (is_yat(VAR)) {
+    bias = p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
     eps = softplus_precise(p.eps_raw[h]);
   } else if (VAR == kStau) {
     tau = softplus_precise(p.log_tau[h]) + 1.f;
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
-      VAR == kYat ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
-  if (VAR == kYat) {
+      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+  if (is_yat(VAR)) {
     f32x16 g = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
         kreg[i] = ld128(rk, off);
       }
     }
-    if (VAR == kYat && gtid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * gtid);
+    if (is_yat(VAR) && gtid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * gtid);
   };
   auto store_k = [&](int t) {
     unsigned short* K = sK[t & 1];
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
         *(u32x4*)&K[row * KLD + 8 * c] = kreg[i];
       }
     }
-    if (VAR == kYat && gtid < BN / 4) *(f32x4*)&sNK[t % 3][4 * gtid] = nkreg;
+    if (is_yat(VAR) && gtid < BN / 4) *(f32x4*)&sNK[t % 3][4 * gtid] = nkreg;
   };
   auto load_v = [&](int k0) {
 #pragma unroll
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           sacc[kb][r] = e;
           mass += e;
         }
-    } else if (VAR == kYat) {
+    } else if (is_yat(VAR)) {
       const float* NK = sNK[t % 3];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
             const float u = sacc[kb][r0 + r] + bias;
-            float kap = u * u * rc[r];
+            float kap = yat_numerator<VAR>(u, p.yat_power) * rc[r];
             if (MASK) kap = allowed(kb, r0 + r) ? kap : 0.f;
             sacc[kb][r0 + r] = kap;
             mass += kap;
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
     load_v(0);
   }
   __syncthreads();
-  if (VAR == kYat) nq = sNQ[32 * w + col];
+  if (is_yat(VAR)) nq = sNQ[32 * w + col];
 
   const int n_phases = 2 * n_tiles + 2;
   for (int ph = 0; ph < n_phases; ++ph) {
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   const float mx_all = pair_max(mx);
   if (VAR == kSoftmax) mass_all *= __builtin_amdgcn_exp2f(mref - mx_all);  // relative to the max
   float inv;
-  if (VAR == kYat) inv = 1.f / (mass_all + 1e-9f);
+  if (is_yat(VAR)) inv = 1.f / (mass_all + 1e-9f);
   else if (VAR == kSoftmax) inv = 1.f / mass_all;
   else inv = mass_all > 0.f ? 1.f / mass_all : 0.f;
   // softmax: O holds sum exp2(x - mref) v; mass_all is relative to mx_all
@@ -642,8 +642,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 
   // Per-head scalars (prologue).
   float bias = 0.f, eps = 0.f, tau = 0.f;
-  if (VAR == kYat) {
-    bias = softplus_precise(p.b_raw[h]);
+  if (is_yat(VAR)) {
+    bias = p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
     eps = softplus_precise(p.eps_raw[h]);
   } else if (VAR == kStau) {
     tau = softplus_precise(p.log_tau[h]) + 1.f;
@@ -663,8 +663,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
-      VAR == kYat ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
-  if (VAR == kYat) {
+      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+  if (is_yat(VAR)) {
     f32x16 g = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
@@ -702,7 +702,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         }
       }
     }
-    if (VAR == kYat && tid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
+    if (is_yat(VAR) && tid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
   };
 
   auto store_tile = [&](int buf) {
@@ -735,7 +735,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         }
       }
     }
-    if (VAR == kYat && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
+    if (is_yat(VAR) && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
   };
 
   f32x16 o[DB];
@@ -798,7 +798,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           sacc[kb][r] = e;
           mass += e;
         }
-    } else if (VAR == kYat) {
+    } else if (is_yat(VAR)) {
       const float* NK = sNK[buf];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -821,7 +821,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           const float s = sacc[kb][r];
           const float d2 = fmaf(-2.f, s, nq + nk[r]);
           const float u = s + bias;
-          float kap = u * u * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
+          float kap = yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
           if (MASK) kap = allowed(kb, r) ? kap : 0.f;
           sacc[kb][r] = kap;
           mass += kap;
@@ -878,7 +878,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   store_tile(0);
   if (n_tiles > 1) load_tile(BN);
   __syncthreads();
-  if (VAR == kYat) nq = sNQ[32 * w + col];
+  if (is_yat(VAR)) nq = sNQ[32 * w + col];
 
   for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * BN, buf = t & 1;
@@ -902,7 +902,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const float mx_all = pair_max(mx);
   if (VAR == kSoftmax) mass_all *= __builtin_amdgcn_exp2f(mref - mx_all);  // relative to the max
   float inv;
-  if (VAR == kYat) inv = 1.f / (mass_all + 1e-9f);
+  if (is_yat(VAR)) inv = 1.f / (mass_all + 1e-9f);
   else if (VAR == kSoftmax) inv = 1.f / mass_all;
   else inv = mass_all > 0.f ? 1.f / mass_all : 0.f;
   // softmax: O holds sum exp2(x - mref) v; mass_all is relative to mx_all
@@ -939,7 +939,7 @@ template <int VAR, int DV>
 hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   constexpr int DK = SFS_DK;
   constexpr int BN = SFS_BN;
-  if (VAR == kYat) {
+  if (is_yat(VAR)) {
     const dim3 grid((p.Tk + 127) / 128, p.Hkv, p.B);
     hipLaunchKernelGGL(row_norms_bf16<DK>, grid, dim3(256), 0, stream,
                        (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk, p.nk);
@@ -982,7 +982,7 @@ hipError_t launch_dv(const Problem& p, hipStream_t stream) {
 hipError_t SFS_CAT(launch_bf16_dk, SFS_DK)(const Problem& p, hipStream_t stream) {
   switch (p.variant) {
     case kSoftmax: return launch_dv<kSoftmax>(p, stream);
-    case kYat: return launch_dv<kYat>(p, stream);
+    case kYat: return p.yat_power > 1 ? launch_dv<kYatPow>(p, stream) : launch_dv<kYat>(p, stream);
     case kStau: return launch_dv<kStau>(p, stream);
   }
   return hipErrorInvalidValue;

@@ -50,8 +50,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(Problem p) {
   __syncthreads();
 
   float bias = 0.f, eps = 0.f, tau = 0.f, nq = 0.f;
-  if (VAR == kYat) {
-    bias = softplus_f(p.b_raw[h]);
+  if (is_yat(VAR)) {
+    bias = p.yat_bias_free ? 0.f : softplus_f(p.b_raw[h]);
     eps = softplus_f(p.eps_raw[h]);
     for (int d = 0; d < dk; ++d) nq = fmaf(sQ[d], sQ[d], nq);
   } else if (VAR == kStau) {
@@ -76,11 +76,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(Problem p) {
       }
     }
     float w = 0.f;
-    if (VAR == kYat) {
+    if (is_yat(VAR)) {
       if (allowed) {
         const float d2 = fmaf(-2.f, s, nq + nk);
         const float u = s + bias;
-        w = (u * u) / (fmaxf(d2, 0.f) + eps);
+        w = yat_numerator<VAR>(u, p.yat_power) / (fmaxf(d2, 0.f) + eps);
         m = fmaxf(m, w);
       }
       mass += w;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(Problem p) {
   const float mass_all = wave_sum(mass);
   const float mx = VAR == kSoftmax ? m : wave_max(m);
   float inv;
-  if (VAR == kYat) inv = 1.f / (mass_all + 1e-9f);
+  if (is_yat(VAR)) inv = 1.f / (mass_all + 1e-9f);
   else if (VAR == kSoftmax) inv = 1.f / mass_all;
   else inv = mass_all > 0.f ? 1.f / mass_all : 0.f;
   float* orow = (float*)p.out + (int64_t)b * p.os[0] + (int64_t)h * p.os[1] + (int64_t)i * p.os[2];
@@ -135,7 +135,12 @@ hipError_t launch_f32(const Problem& p, hipStream_t stream) {
   const unsigned n = (unsigned)((int64_t)p.B * p.Hq * p.Tq);
   switch (p.variant) {
     case kSoftmax: hipLaunchKernelGGL(attn_fwd_f32<kSoftmax>, dim3(n), dim3(64), 0, stream, p); break;
-    case kYat: hipLaunchKernelGGL(attn_fwd_f32<kYat>, dim3(n), dim3(64), 0, stream, p); break;
+    case kYat:
+      if (p.yat_power > 1)
+        hipLaunchKernelGGL(attn_fwd_f32<kYatPow>, dim3(n), dim3(64), 0, stream, p);
+      else
+        hipLaunchKernelGGL(attn_fwd_f32<kYat>, dim3(n), dim3(64), 0, stream, p);
+      break;
     case kStau: hipLaunchKernelGGL(attn_fwd_f32<kStau>, dim3(n), dim3(64), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }

@@ -7,7 +7,24 @@
 
 namespace sfs {
 
-enum Variant : int { kSoftmax = 0, kYat = 1, kStau = 2 };
+// kYatPow is internal: the Yat map with the numerator raised to a power
+// m >= 2 (m = yat_power, a runtime value); kYat is the m = 1 kernel.
+enum Variant : int { kSoftmax = 0, kYat = 1, kStau = 2, kYatPow = 3 };
+__host__ __device__ constexpr bool is_yat(int v) { return v == kYat || v == kYatPow; }
+
+// Yat numerator (s + b)^(2m) from u = s + b: u^2 for kYat, (u^2)^m for kYatPow.
+template <int VAR>
+__device__ __forceinline__ float yat_numerator(float u, int m) {
+  const float u2 = u * u;
+  if constexpr (VAR == kYatPow) {
+    float num = u2;
+    for (int i = 1; i < m; ++i) num *= u2;
+    return num;
+  } else {
+    (void)m;
+    return u2;
+  }
+}
 
 // Row pitch (in floats) of the Yat |k|^2 workspace per (batch, kv head):
 // T_k rounded up to 64, so a 64-key tile never reads past its slice.
@@ -31,7 +48,9 @@ struct Problem {
   int B, Hq, Hkv, Tq, Tk, dk, dv;
   int variant;
   int causal;
-  int block_rows;  // 0: choose by grid size; 64, 128, 256: force that kernel
+  int block_rows;     // 0: choose by grid size; 64, 128, 256: force that kernel
+  int yat_power;      // Yat numerator power m >= 1 ((s + b)^(2m))
+  int yat_bias_free;  // Yat: b = 0 exactly (b_raw not read)
 };
 
 // Fused forward for fp32 storage (vector-ALU path).

@@ -43,8 +43,15 @@ def to_device(inp, tied_copy=True):
     return q, k, v, prm
 
 
-def run_gpu(q, k, v, prm, variant, causal, **kw):
-    out, mass, mx = attn.attn_fwd(q, k, v, variant, causal=causal, **prm, **kw)
+def run_gpu(q, k, v, prm, variant, causal, yat_opts=None, **kw):
+    """One call through the C ABI: attn_fwd, or attn_fwd_yat when ``yat_opts``
+    = (power, bias_free) is given."""
+    if yat_opts is not None:
+        out, mass, mx = attn.attn_fwd_yat(q, k, v, prm["b_raw"], prm["eps_raw"],
+                                          power=yat_opts[0], bias_free=yat_opts[1],
+                                          causal=causal, **kw)
+    else:
+        out, mass, mx = attn.attn_fwd(q, k, v, variant, causal=causal, **prm, **kw)
     torch.cuda.synchronize()
     return out, mass, mx
 
@@ -53,15 +60,19 @@ def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def oracle_full(inp, variant, causal):
+def _yat_kw(yat_opts):
+    return {} if yat_opts is None else dict(yat_power=yat_opts[0], yat_bias_free=yat_opts[1])
+
+
+def oracle_full(inp, variant, causal, yat_opts=None):
     q, k, v = inp.f64()
-    return oracle.attn_fwd_np(q, k, v, variant, causal=causal,
+    return oracle.attn_fwd_np(q, k, v, variant, causal=causal, **_yat_kw(yat_opts),
                               **{n: a.astype(np.float64) for n, a in inp.params().items()})
 
 
-def oracle_rows(inp, variant, causal, rows):
+def oracle_rows(inp, variant, causal, rows, yat_opts=None):
     q, k, v = inp.f64()
-    return oracle.attn_fwd_c(q, k, v, variant, causal=causal, rows=rows,
+    return oracle.attn_fwd_c(q, k, v, variant, causal=causal, rows=rows, **_yat_kw(yat_opts),
                              **{n: a.astype(np.float64) for n, a in inp.params().items()})
 
 

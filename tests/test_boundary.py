@@ -140,3 +140,23 @@ def test_status_strings():
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_PARAM, ERR_WS, ERR_HIP):
         assert lib.attn_status_string(code)
     assert lib.attn_status_string(99) == b"unknown status"
+
+
+def call_yat(d, opts, b=BR, e=ER, causal=1):
+    return attn.call_raw_yat(d, A, K, V, b, e, opts, causal, O, M, X, W, 1 << 20, 0)
+
+
+@pytest.mark.parametrize("opts,b,status", [
+    (attn.AttnYatOpts(0, 0), BR, ERR_UNSUP),                       # power below 1
+    (attn.AttnYatOpts(attn.ATTN_YAT_MAX_POWER + 1, 0), BR, ERR_UNSUP),
+    (attn.AttnYatOpts(2, 0), 0, ERR_PARAM),                        # b_raw needed
+    (attn.AttnYatOpts(2, 1), 0, ERR_HIP),                          # bias-free: b_raw unused
+    (None, BR, ERR_HIP),                                           # NULL opts: standard kernel
+    (attn.AttnYatOpts(attn.ATTN_YAT_MAX_POWER, 1), BR, ERR_HIP)])
+def test_yat_options_validation(opts, b, status):
+    assert call_yat(desc(), opts, b=b) == status
+
+
+def test_yat_options_need_eps_and_desc():
+    assert call_yat(desc(), attn.AttnYatOpts(1, 1), e=0) == ERR_PARAM
+    assert call_yat(None, None) == ERR_NULL

@@ -25,13 +25,15 @@ def v_max(inp):
 BLOCK_ROWS = (0, 64, 128, 256)
 
 
-def full_check(inp, variant, causal, label, block_rows=(0,)):
+def full_check(inp, variant, causal, label, block_rows=(0,), yat_opts=None):
     say(f"[gpu] {label} {variant} causal={causal} shape B{inp.wl.B} Hq{inp.wl.Hq} "
-        f"Hkv{inp.wl.Hkv} Tq{inp.wl.Tq} Tk{inp.wl.Tk} dk{inp.wl.dk} dv{inp.wl.dv} {inp.wl.dtype}")
+        f"Hkv{inp.wl.Hkv} Tq{inp.wl.Tq} Tk{inp.wl.Tk} dk{inp.wl.dk} dv{inp.wl.dv} {inp.wl.dtype}"
+        f"{'' if yat_opts is None else f' yat_opts={yat_opts}'}")
     q, k, v, prm = to_device(inp)
-    ref = oracle_full(inp, variant, causal)
+    ref = oracle_full(inp, variant, causal, yat_opts)
     for rows in block_rows:
-        got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal, block_rows=rows)]
+        got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal, yat_opts=yat_opts,
+                                         block_rows=rows)]
         check(inp.wl.dtype, got, ref, v_max(inp), f"{label}/{variant}/rows{rows}",
               v_rms=v_rms(inp))
 
@@ -91,6 +93,58 @@ def test_medium_shapes_fp32(variant, shape):
 def test_tied_medium_yat(dtype):
     inp = make_custom(1, 3, 3, 300, 300, 128, 128, dtype, True, seed=9, qk_std=2.0, tied=True)
     full_check(inp, "yat", True, "tied_medium", BLOCK_ROWS if dtype == "bf16" else (0,))
+
+
+# ------------------------------------------- Yat options (attn_fwd_yat)
+
+YAT_OPTS = [(2, False), (3, True), (1, True)]
+
+
+@pytest.mark.parametrize("opts", YAT_OPTS, ids=lambda o: f"m{o[0]}{'_nobias' if o[1] else ''}")
+@pytest.mark.parametrize("shape", [MEDIUM[0], MEDIUM[1], MEDIUM[3], MEDIUM[6]],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_yat_options_bf16(shape, opts):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=15, qk_std=1.0)
+    full_check(inp, "yat", causal, "yat_opts", BLOCK_ROWS, yat_opts=opts)
+
+
+@pytest.mark.parametrize("opts", YAT_OPTS, ids=lambda o: f"m{o[0]}{'_nobias' if o[1] else ''}")
+def test_yat_options_fp32(opts):
+    inp = make_custom(1, 2, 1, 100, 100, 32, 64, "f32", True, seed=16)
+    full_check(inp, "yat", True, "yat_opts_f32", yat_opts=opts)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_yat_power_tied_peak(dtype):
+    # k := q: the diagonal carries the peak (|q|^2 + b)^(2m) / eps
+    inp = make_custom(1, 2, 2, 160, 160, 64, 64, dtype, True, seed=17, qk_std=1.0, tied=True)
+    full_check(inp, "yat", True, "yat_pow_tied", BLOCK_ROWS if dtype == "bf16" else (0,),
+               yat_opts=(2, False))
+
+
+def test_yat_options_full_size_sampled():
+    wl = WORKLOADS["cross"]
+    inp = make_inputs(wl)
+    say("[gpu] full-size cross yat power 2")
+    q, k, v, prm = to_device(inp)
+    out, mass, mx = run_gpu(q, k, v, prm, "yat", wl.causal, yat_opts=(2, False))
+    rows = sample_rows(wl.B, wl.Hq, wl.Tq)
+    ref = oracle_rows(inp, "yat", wl.causal, rows, yat_opts=(2, False))
+    flat = lambda t, d: to_np(t).reshape(-1, d)[rows].reshape(-1) if d == 1 else \
+        to_np(t).reshape(-1, d)[rows]
+    check(wl.dtype, (flat(out, wl.dv), flat(mass, 1), flat(mx, 1)), ref, v_max(inp),
+          "cross/yat_m2", v_rms=v_rms(inp))
+
+
+def test_yat_default_options_match_attn_fwd():
+    # opts (1, no bias-free) is the standard kernel, bit for bit
+    inp = make_custom(2, 4, 2, 300, 300, 128, 128, "bf16", True, seed=18)
+    q, k, v, prm = to_device(inp)
+    a = run_gpu(q, k, v, prm, "yat", True)
+    b = run_gpu(q, k, v, prm, "yat", True, yat_opts=(1, False))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 # --------------------------------------------------------------- edge cases

@@ -13,7 +13,8 @@ IMPLS = ["c", "np"]
 LN2 = math.log(2.0)
 
 
-def run(impl, q, k, v, variant, causal=False, b_raw=None, eps_raw=None, log_tau=None):
+def run(impl, q, k, v, variant, causal=False, b_raw=None, eps_raw=None, log_tau=None,
+        yat_power=1, yat_bias_free=False):
     """Oracle on single-head 2-D inputs (Tq x dk, Tk x dk, Tk x dv) or 4-D."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     two_d = q.ndim == 2
@@ -24,8 +25,9 @@ def run(impl, q, k, v, variant, causal=False, b_raw=None, eps_raw=None, log_tau=
     eps_raw = np.zeros(Hq) if eps_raw is None else np.broadcast_to(np.asarray(eps_raw, float), (Hq,))
     log_tau = np.zeros(Hq) if log_tau is None else np.broadcast_to(np.asarray(log_tau, float), (Hq,))
     fn = oracle.attn_fwd_c if impl == "c" else oracle.attn_fwd_np
+    opts = {} if variant != "yat" else dict(yat_power=yat_power, yat_bias_free=yat_bias_free)
     out, mass, mx = fn(q, k, v, variant, b_raw=b_raw, eps_raw=eps_raw, log_tau=log_tau,
-                       causal=causal)
+                       causal=causal, **opts)
     if two_d:
         return out[0, 0], mass[0, 0], mx[0, 0]
     return out, mass, mx
@@ -233,6 +235,62 @@ def test_yat_mass_is_sum_of_pair_scores(impl):
 
 
 # --------------------------------------------------------------------------
+# Yat kernel-family options ("The Kernel Between the Roles", "The run"): the
+# numerator power (q.k + b)^(2m) and the b = 0 ablation
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("bias_free", [False, True])
+def test_yat_power_peak_at_query(impl, m, bias_free):
+    # a key equal to its query: distance 0, so kappa = (|q|^2 + b)^(2m) / eps
+    rng = np.random.default_rng(40 + m)
+    q = rng.standard_normal((1, 5))
+    nq = (q @ q.T).item()
+    _, mass, mx = run(impl, q, q, [[1.0]], "yat", b_raw=0.0, eps_raw=0.0, yat_power=m,
+                      yat_bias_free=bias_free)
+    b = 0.0 if bias_free else LN2
+    peak = (nq + b) ** (2 * m) / LN2
+    assert abs(mass[0] - peak) <= 1e-13 * peak and mx[0] == mass[0]
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_yat_power_hand_values(impl):
+    b, e = math.log1p(math.exp(0.5)), math.log1p(math.exp(-1.0))
+    # q = (1, 0), k = (1, 1): q.k = 1, |q - k|^2 = 1
+    # q = (2, -1), k = (-1, 3): q.k = -5, |q - k|^2 = 25
+    for q, k, dot_, d2 in (([[1.0, 0.0]], [[1.0, 1.0]], 1.0, 1.0),
+                           ([[2.0, -1.0]], [[-1.0, 3.0]], -5.0, 25.0)):
+        for m in (2, 3, 4):
+            _, mass, _ = run(impl, q, k, [[1.0]], "yat", b_raw=0.5, eps_raw=-1.0, yat_power=m)
+            want = (dot_ + b) ** (2 * m) / (d2 + e)
+            assert abs(mass[0] - want) <= 1e-14 * want
+            # the bias-free kernel ignores b_raw
+            _, mass0, _ = run(impl, q, k, [[1.0]], "yat", b_raw=0.5, eps_raw=-1.0, yat_power=m,
+                              yat_bias_free=True)
+            want0 = dot_ ** (2 * m) / (d2 + e)
+            assert abs(mass0[0] - want0) <= 1e-14 * want0
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_yat_bias_free_equals_softplus_minus_infinity(impl):
+    # the explicit flag and b_raw = -inf are the same kernel (b = 0 exactly)
+    rng = np.random.default_rng(44)
+    q, k, v = rng.standard_normal((4, 3)), rng.standard_normal((6, 3)), rng.standard_normal((6, 2))
+    a = run(impl, q, k, v, "yat", b_raw=3.0, eps_raw=-0.5, yat_bias_free=True)
+    c = run(impl, q, k, v, "yat", b_raw=-np.inf, eps_raw=-0.5)
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_yat_bias_free_orthogonal_pair_scores_zero_any_power(impl, m):
+    out, mass, mx = run(impl, [[1.0, 0.0]], [[0.0, 1e-3]], [[7.0, -3.0]], "yat", b_raw=2.0,
+                        eps_raw=0.0, yat_power=m, yat_bias_free=True)
+    assert mass[0] == 0.0 and mx[0] == 0.0 and np.all(out == 0.0)
+
+
+# --------------------------------------------------------------------------
 # s^tau: the core formula and its softmax identity ("s^tau" forum post)
 
 def _tau_for(t):
@@ -309,7 +367,8 @@ def test_gqa_equals_repeated_kv(impl, variant):
         np.testing.assert_array_equal(x, y)
 
 
-def brute_force(q, k, v, variant, b_raw, eps_raw, log_tau, causal):
+def brute_force(q, k, v, variant, b_raw, eps_raw, log_tau, causal, yat_power=1,
+                yat_bias_free=False):
     """Pure-Python loops over 4-D nested lists; tiny inputs only."""
     B, Hq, Tq, dk = q.shape
     Hkv, Tk, dv = k.shape[1], k.shape[2], v.shape[3]
@@ -326,7 +385,11 @@ def brute_force(q, k, v, variant, b_raw, eps_raw, log_tau, causal):
                     if variant == "yat":
                         nq = sum(float(x) ** 2 for x in q[b, h, i])
                         nk = sum(float(x) ** 2 for x in k[b, hk, j])
-                        sc[j] = (d + sp(b_raw[h])) ** 2 / (max(nq + nk - 2 * d, 0.0) + sp(eps_raw[h]))
+                        bb = 0.0 if yat_bias_free else sp(b_raw[h])
+                        num = 1.0
+                        for _ in range(yat_power):
+                            num *= (d + bb) * (d + bb)
+                        sc[j] = num / (max(nq + nk - 2 * d, 0.0) + sp(eps_raw[h]))
                     else:
                         sc[j] = d / math.sqrt(dk)
                 if variant == "yat":
@@ -365,6 +428,23 @@ def test_brute_force_tiny(variant, shape):
             np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("opts", [(2, False), (3, True), (1, True)])
+def test_brute_force_tiny_yat_options(opts):
+    m, bias_free = opts
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = 1, 4, 2, 5, 5, 3, 2, True
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((B, Hq, Tq, dk))
+    k = rng.standard_normal((B, Hkv, Tk, dk))
+    v = rng.standard_normal((B, Hkv, Tk, dv))
+    prm = dict(b_raw=rng.uniform(-1, 1, Hq), eps_raw=rng.uniform(-3, 0, Hq), log_tau=None)
+    ref = brute_force(q, k, v, "yat", causal=causal, yat_power=m, yat_bias_free=bias_free, **prm)
+    for impl in IMPLS:
+        got = run(impl, q, k, v, "yat", causal=causal, yat_power=m, yat_bias_free=bias_free,
+                  **prm)
+        for x, y in zip(got, ref):
+            np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("variant", ["softmax", "yat", "stau"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_c_and_numpy_oracles_agree(variant, causal):
@@ -395,3 +475,5 @@ def test_oracle_rejects_bad_arguments():
         oracle.attn_fwd_c(q, k, v, "softmax", causal=True)
     with pytest.raises(ValueError):      # out-of-range row id
         oracle.attn_fwd_c(q, k, v, "softmax", rows=[3])
+    with pytest.raises(ValueError):      # Yat numerator power below 1
+        oracle.attn_fwd_c(q, k, v, "yat", b_raw=np.zeros(1), eps_raw=np.zeros(1), yat_power=0)
