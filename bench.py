@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--block-rows", type=int, default=0, choices=(0, 64, 128, 256),
                     help="query rows per workgroup of the bf16 kernel (0: the library's "
                          "choice from the grid size)")
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="key chunks per workgroup of the small-grid kernels (0: the library's "
+                         "choice, 1: none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -168,7 +171,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ws = {}
     for var in ("yat", "softmax", "stau"):
-        n = attn.workspace_bytes(q, k, v, var)
+        n = attn.workspace_bytes(q, k, v, var, args.block_rows, args.kv_splits)
         ws[var] = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
 
     def call(var):
@@ -179,7 +182,7 @@ def main():
             it[0] += 1
             attn.attn_fwd(q_, k_, v_, var, causal=wl.causal, out=o_, mass=m_, max_score=x_,
                           workspace=ws[var], stream=stream.cuda_stream,
-                          block_rows=args.block_rows, **prm)
+                          block_rows=args.block_rows, kv_splits=args.kv_splits, **prm)
         return run
 
     flops = alg_flops(wl)
@@ -212,6 +215,7 @@ def main():
                                f"{'causal' if wl.causal else 'non-causal'}",
                    "variant": primary, "global_batch": wl.B, "seq_len": wl.Tq,
                    "input_sets_rotated": len(sets), "block_rows": args.block_rows,
+                   "kv_splits": args.kv_splits,
                    "parallelism": "none (1 GPU)"},
         "roofline": {**roof,
                      "traffic": recorded_traffic(wl.name, primary),

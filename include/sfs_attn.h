@@ -63,10 +63,10 @@ enum {
   ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,       /* a size is negative or zero where it may not be,
                                 Hq % Hkv != 0, or causal with T_q != T_k */
-  ATTN_ERR_UNSUPPORTED = -3, /* dtype, variant, head size or block_rows not
-                                built; a base pointer or stride breaks the
-                                16-byte alignment rule; a per-head offset
-                                exceeds 2^31 elements */
+  ATTN_ERR_UNSUPPORTED = -3, /* dtype, variant, head size, block_rows or
+                                kv_splits not built; a base pointer or stride
+                                breaks the 16-byte alignment rule; a per-head
+                                offset exceeds 2^31 elements */
   ATTN_ERR_PARAM = -4,       /* a per-head parameter the variant needs is NULL */
   ATTN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
   ATTN_ERR_HIP = -6          /* the HIP runtime failed (no device, launch
@@ -94,6 +94,18 @@ typedef struct {
   int64_t k_stride[3];
   int64_t v_stride[3];
   int64_t o_stride[3];
+  /* Key splits of the bf16 64- and 128-row kernels.  When a problem has too
+   * few query tiles to fill the device (decode, short query blocks against
+   * long keys), each workgroup's keys are cut into chunks of whole tiles that
+   * run in parallel; each chunk writes unnormalised partials (O, mass,
+   * maximum, and for softmax the reference maximum) to the workspace, and a
+   * second kernel merges them: plain sums for Yat and s^tau, whose weights
+   * need no running maximum, and the log-sum-exp merge for softmax.
+   * 0 lets the library choose; 1 switches splitting off; 2 .. 64 force that
+   * many chunks (bf16 only, not with block_rows = 256).  Results differ from
+   * the unsplit ones only in the order of fp32 additions. */
+  int32_t kv_splits;
+  int32_t reserved; /* must be 0 */
 } attn_desc;
 
 /* Fill *desc for densely packed [B,H,T,d] tensors.  Returns ATTN_OK or
@@ -101,9 +113,10 @@ typedef struct {
 int attn_desc_init(attn_desc* desc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq,
                    int64_t Tk, int64_t dk, int64_t dv, int32_t dtype);
 
-/* Device workspace, in bytes, that attn_fwd needs for this problem and map
- * (ATTN_YAT keeps fp32 |k|^2 per key row there; the others need none).
- * Returns 0 when none is needed or the description is invalid. */
+/* Device workspace, in bytes, that attn_fwd needs for this problem and map:
+ * fp32 |k|^2 per key row for ATTN_YAT with bf16 storage, and, when the keys
+ * are split (see kv_splits), fp32 partials of 4 (d_v + 4) bytes per query row
+ * and chunk.  Returns 0 when none is needed or the description is invalid. */
 size_t attn_fwd_workspace_bytes(const attn_desc* desc, int variant);
 
 /* Attention forward.

@@ -37,7 +37,8 @@ class AttnDesc(ctypes.Structure):
                 ("Tq", ctypes.c_int64), ("Tk", ctypes.c_int64), ("dk", ctypes.c_int64),
                 ("dv", ctypes.c_int64), ("dtype", ctypes.c_int32), ("block_rows", ctypes.c_int32),
                 ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
-                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+                ("kv_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class AttnYatOpts(ctypes.Structure):
@@ -94,9 +95,11 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def make_desc(q, k, v, out=None, block_rows=0) -> AttnDesc:
+def make_desc(q, k, v, out=None, block_rows=0, kv_splits=0) -> AttnDesc:
     """Descriptor from 4-D tensors (strides in elements, last axis contiguous).
-    ``block_rows`` 0 lets the library pick the bf16 kernel; 64/128/256 force one."""
+    ``block_rows`` 0 lets the library pick the bf16 kernel; 64/128/256 force one.
+    ``kv_splits`` 0 lets the library decide whether to split the keys; 1 never;
+    n >= 2 forces n chunks."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t is None:
             continue
@@ -112,14 +115,16 @@ def make_desc(q, k, v, out=None, block_rows=0) -> AttnDesc:
     d.B, d.Hq, d.Hkv, d.Tq, d.Tk, d.dk, d.dv = B, Hq, Hkv, Tq, Tk, dk, dv
     d.dtype = _dtype_code(q)
     d.block_rows = int(block_rows)
+    d.kv_splits = int(kv_splits)
     for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
         if t is not None:
             getattr(d, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
     return d
 
 
-def workspace_bytes(q, k, v, variant) -> int:
-    return int(load_library().attn_fwd_workspace_bytes(ctypes.byref(make_desc(q, k, v)),
+def workspace_bytes(q, k, v, variant, block_rows=0, kv_splits=0) -> int:
+    d = make_desc(q, k, v, None, block_rows, kv_splits)
+    return int(load_library().attn_fwd_workspace_bytes(ctypes.byref(d),
                                                        VARIANTS.get(variant, variant)))
 
 
@@ -127,7 +132,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_rows):
+def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_rows,
+             kv_splits=0):
     lib = load_library()
     B, Hq, Tq, _ = q.shape
     dv = v.shape[3]
@@ -141,7 +147,7 @@ def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_ro
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
                               or t.numel() != B * Hq * Tq):
             raise ValueError(f"{name} must be a contiguous float32 tensor of B*Hq*Tq elements")
-    desc = make_desc(q, k, v, out, block_rows)
+    desc = make_desc(q, k, v, out, block_rows, kv_splits)
     need = int(lib.attn_fwd_workspace_bytes(ctypes.byref(desc), variant))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -152,7 +158,8 @@ def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_ro
 
 
 def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False, out=None,
-             mass=None, max_score=None, workspace=None, stream=None, block_rows=0):
+             mass=None, max_score=None, workspace=None, stream=None, block_rows=0,
+             kv_splits=0):
     """Enqueue the fused forward; returns (out, mass, max_score).
 
     Outputs that are not given are allocated (out like q with d_v columns;
@@ -161,7 +168,7 @@ def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=Fa
     on q's device.  Raises AttnError with the library's status on failure."""
     variant = VARIANTS.get(variant, variant)
     lib, desc, out, mass, max_score, workspace, ws_bytes, stream = _prepare(
-        q, k, v, variant, out, mass, max_score, workspace, stream, block_rows)
+        q, k, v, variant, out, mass, max_score, workspace, stream, block_rows, kv_splits)
     st = lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), variant, _ptr(b_raw),
                       _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(out), _ptr(mass),
                       _ptr(max_score), _ptr(workspace), ws_bytes,
@@ -172,12 +179,13 @@ def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=Fa
 
 
 def attn_fwd_yat(q, k, v, b_raw=None, eps_raw=None, power=1, bias_free=False, causal=False,
-                 out=None, mass=None, max_score=None, workspace=None, stream=None, block_rows=0):
+                 out=None, mass=None, max_score=None, workspace=None, stream=None, block_rows=0,
+                 kv_splits=0):
     """The Yat forward with kernel-family options: numerator (q.k + b)^(2 power),
     and b = 0 exactly when ``bias_free`` (b_raw then unused).  Otherwise as
     ``attn_fwd(..., "yat", ...)``."""
     lib, desc, out, mass, max_score, workspace, ws_bytes, stream = _prepare(
-        q, k, v, ATTN_YAT, out, mass, max_score, workspace, stream, block_rows)
+        q, k, v, ATTN_YAT, out, mass, max_score, workspace, stream, block_rows, kv_splits)
     opts = AttnYatOpts(int(power), int(bool(bias_free)))
     st = lib.attn_fwd_yat(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(b_raw),
                           _ptr(eps_raw), ctypes.byref(opts), int(bool(causal)), _ptr(out),

@@ -36,6 +36,7 @@ def _hipcc() -> str:
 def _units():
     units = [("attn_api", "attn_api.cpp", [])]
     units.append(("attn_f32", "attn_f32.hip", []))
+    units.append(("attn_combine", "attn_combine.hip", []))
     for dk in (16, 32, 64, 128):
         units.append((f"attn_bf16_dk{dk}", "attn_bf16.hip", [f"-DSFS_DK={dk}"]))
     return units

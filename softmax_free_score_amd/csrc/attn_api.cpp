@@ -36,6 +36,31 @@ bool strides_ok(const int64_t s[3], int64_t rows, int64_t d, int64_t elem) {
   return span < (int64_t(1) << 31);
 }
 
+// Workspace layout of the bf16 path: Yat |k|^2 rows, then (key splits) the
+// partials, each region 256-byte aligned.
+struct WsLayout {
+  sfs::Plan plan;
+  size_t nk_bytes, part_off, total;
+};
+WsLayout ws_layout(const attn_desc* d, int variant, int causal) {
+  WsLayout w{};
+  w.plan = sfs::make_plan(d->B, d->Hq, d->Tq, d->Tk, causal, d->block_rows, d->kv_splits);
+  w.nk_bytes = variant == ATTN_YAT ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
+  w.part_off = (w.nk_bytes + 255) / 256 * 256;
+  w.total = w.nk_bytes;
+  if (w.plan.splits > 1)
+    w.total = w.part_off + (size_t)w.plan.splits * (size_t)(d->B * d->Hq * d->Tq) *
+                               (size_t)(d->dv + 4) * sizeof(float);
+  return w;
+}
+// The plan depends on the mask (a causal problem needs 4x more 256-row
+// workgroups before it takes that kernel), which the workspace query does not
+// know: size for the larger of the two.
+size_t ws_need(const attn_desc* d, int variant) {
+  const size_t a = ws_layout(d, variant, 0).total, c = ws_layout(d, variant, 1).total;
+  return a > c ? a : c;
+}
+
 int validate(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
              const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
              const void* out, const float* mass, const float* max_score, const void* ws,
@@ -74,6 +99,11 @@ int validate(const attn_desc* d, const void* q, const void* k, const void* v, in
   if (d->block_rows != 0 && (d->dtype != ATTN_BF16 || (d->block_rows != 64 &&
                              d->block_rows != 128 && d->block_rows != 256))) {
     set_error("block_rows must be 0, or 64, 128 or 256 with bf16 storage");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (d->kv_splits < 0 || d->kv_splits > sfs::kMaxKvSplits || d->reserved != 0 ||
+      (d->kv_splits > 1 && (d->dtype != ATTN_BF16 || d->block_rows == 256))) {
+    set_error("kv_splits must be 0 .. 64; more than 1 needs bf16 and a 64- or 128-row kernel");
     return ATTN_ERR_UNSUPPORTED;
   }
   if (!head_dim_ok(d->dk) || !head_dim_ok(d->dv)) {
@@ -134,9 +164,9 @@ int attn_desc_init(attn_desc* d, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq,
 }
 
 size_t attn_fwd_workspace_bytes(const attn_desc* d, int variant) {
-  if (!d || variant != ATTN_YAT || d->dtype != ATTN_BF16) return 0;
-  if (d->B <= 0 || d->Hkv <= 0 || d->Tk <= 0) return 0;
-  return (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * sizeof(float);
+  if (!d || d->dtype != ATTN_BF16) return 0;
+  if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0 || d->dv <= 0) return 0;
+  return ws_need(d, variant);
 }
 
 }  // extern "C"
@@ -167,7 +197,13 @@ int run(const attn_desc* d, const void* q, const void* k, const void* v, int var
   p.Tq = (int)d->Tq; p.Tk = (int)d->Tk; p.dk = (int)d->dk; p.dv = (int)d->dv;
   p.variant = variant;
   p.causal = causal ? 1 : 0;
-  p.block_rows = d->block_rows;
+  p.kv_splits = 1;
+  if (d->dtype == ATTN_BF16) {
+    const WsLayout w = ws_layout(d, variant, p.causal);
+    p.block_rows = w.plan.rows;
+    p.kv_splits = w.plan.splits;
+    if (p.kv_splits > 1) p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part_off);
+  }
   p.yat_power = yat_power;
   p.yat_bias_free = yat_bias_free ? 1 : 0;
 
@@ -184,6 +220,7 @@ int run(const attn_desc* d, const void* q, const void* k, const void* v, int var
         case 64: e = sfs::launch_bf16_dk64(p, s); break;
         default: e = sfs::launch_bf16_dk128(p, s); break;
       }
+      if (e == hipSuccess && p.kv_splits > 1) e = sfs::launch_combine(p, s);
     }
   }
   if (e != hipSuccess) {

@@ -673,6 +673,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
+  // With p.kv_splits > 1 this workgroup takes chunk blockIdx.y of its key
+  // range, in whole tiles, and writes unnormalised partials.
+  const int split = blockIdx.y;
+  const int tps = (n_tiles + p.kv_splits - 1) / p.kv_splits;
+  const int t_begin = min(split * tps, n_tiles);
+  const int t_end = min(t_begin + tps, n_tiles);
 
   // Staging registers for the next key/value tile.
   u32x4 kreg[K_PER_T];
@@ -790,11 +796,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         for (int d = 0; d < DB; ++d) o[d] *= alpha;
         mref = tmax;
       }
+      // (a row with no allowed key so far keeps mref = -inf; its masked
+      // scores must give 0, not -inf - -inf)
+      const float mref_f = fmaxf(mref, -3.0e38f);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(sacc[kb][r] - mref);
+          const float e = __builtin_amdgcn_exp2f(sacc[kb][r] - mref_f);
           sacc[kb][r] = e;
           mass += e;
         }
@@ -873,14 +882,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       }
   };
 
-  // Prologue: tile 0 into stage 0, tile 1 into registers.
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) load_tile(BN);
+  // Prologue: the first tile into its stage, the next into registers.
+  if (t_begin < t_end) {
+    load_tile(t_begin * BN);
+    store_tile(t_begin & 1);
+    if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN);
+  }
   __syncthreads();
   if (is_yat(VAR)) nq = sNQ[32 * w + col];
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = t_begin; t < t_end; ++t) {
     const int k0 = t * BN, buf = t & 1;
     // every key of the tile is in this wave's future: nothing to do
     if (!(p.causal && k0 > qw + 31)) {
@@ -888,11 +899,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       if (need_mask) compute(std::true_type{}, buf, k0);
       else compute(std::false_type{}, buf, k0);
     }
-    if (t + 1 < n_tiles) {
+    if (t + 1 < t_end) {
       // Stage t+1 was last read in iteration t-1, which every wave finished
       // before the barrier that ended it.
       store_tile(buf ^ 1);
-      if (t + 2 < n_tiles) load_tile(k0 + 2 * BN);
+      if (t + 2 < t_end) load_tile(k0 + 2 * BN);
     }
     __syncthreads();
   }
@@ -900,6 +911,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // Epilogue: combine the two lanes that share a query, normalise, store.
   float mass_all = pair_sum(mass);
   const float mx_all = pair_max(mx);
+  if (p.kv_splits > 1) {
+    // partials of this chunk: O (relative to mref for softmax), mass, max, mref
+    if (my_q < p.Tq) {
+      const int64_t R = (int64_t)p.B * p.Hq * p.Tq;
+      const int64_t ri = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
+      float* po = p.part + ((int64_t)split * R + ri) * p.dv;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dv0 = 32 * d + 8 * g4 + 4 * half;
+          if (dv0 < DV) {
+            f32x4 st;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[e] = o[d][4 * g4 + e];
+            *(f32x4*)&po[dv0] = st;
+          }
+        }
+      if (half == 0) {
+        f32x4 st = {mass_all, mx_all, mref, 0.f};
+        *(f32x4*)&p.part[(int64_t)p.kv_splits * R * p.dv + ((int64_t)split * R + ri) * 4] = st;
+      }
+    }
+    return;
+  }
   if (VAR == kSoftmax) mass_all *= __builtin_amdgcn_exp2f(mref - mx_all);  // relative to the max
   float inv;
   if (is_yat(VAR)) inv = 1.f / (mass_all + 1e-9f);
@@ -944,24 +980,17 @@ hipError_t launch_variant(const Problem& p, hipStream_t stream) {
     hipLaunchKernelGGL(row_norms_bf16<DK>, grid, dim3(256), 0, stream,
                        (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk, p.nk);
   }
-  // 256-row ping-pong workgroups when there are enough of them to fill the
-  // chip (and, with a causal mask, to balance tiles of unequal length);
-  // otherwise 128- or 64-row workgroups, several per CU.
+  // p.block_rows and p.kv_splits come from the host plan (make_plan)
   const unsigned bh = (unsigned)p.B * (unsigned)p.Hq;
-  const unsigned n256 = (unsigned)((p.Tq + 255) / 256) * bh;
-  const unsigned n128 = (unsigned)((p.Tq + 127) / 128) * bh;
-  const unsigned n64 = (unsigned)((p.Tq + 63) / 64) * bh;
-  const unsigned cus = 256;
-  int rows = p.block_rows;
-  if (rows == 0) rows = n256 >= (p.causal ? 4 * cus : cus) ? 256 : n128 >= cus ? 128 : 64;
-  if (rows == 256) {
-    hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(n256), dim3(512), 0, stream, p);
-  } else if (rows == 128) {
-    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64>), dim3(n128), dim3(256), 0,
-                       stream, p);
+  const unsigned nq = (unsigned)((p.Tq + p.block_rows - 1) / p.block_rows) * bh;
+  if (p.block_rows == 256) {
+    hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(nq), dim3(512), 0, stream, p);
+  } else if (p.block_rows == 128) {
+    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64>), dim3(nq, p.kv_splits),
+                       dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32>), dim3(n64), dim3(128), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32>), dim3(nq, p.kv_splits),
+                       dim3(128), 0, stream, p);
   }
   return hipGetLastError();
 }

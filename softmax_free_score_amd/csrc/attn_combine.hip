@@ -1,0 +1,81 @@
+// attn_combine.hip -- merges the key-chunk partials of the small-grid kernels.
+//
+// When the keys of a workgroup are split into S chunks, chunk s of query row
+// r leaves O_s (sum over its keys of w_j v_j, unnormalised), its mass m_s, its
+// maximum score x_s and, for softmax, the reference maximum M_s its
+// exponentials are taken against (O_s and m_s are relative to 2^M_s).
+//
+//   Yat, s^tau: the weights need no maximum, so the chunks add:
+//               O = sum O_s, mass = sum m_s, max = max x_s
+//               ("Softmax-Free Attention in JAX/Flax NNX", "One module, two
+//               compatibility functions": out = O / (mass + 1e-9) for Yat;
+//               s^tau forum post, core formula: out = O / mass).
+//   softmax:    the log-sum-exp merge with M = max M_s:
+//               O = sum 2^(M_s - M) O_s, l = sum 2^(M_s - M) m_s, out = O / l,
+//               mass reported relative to the row maximum x = max x_s.
+//
+// One wave per row; lane c holds value columns c and c + 64.  The merge runs
+// over s in order, so the result does not depend on scheduling.
+#include "attn_launch.h"
+
+namespace sfs {
+namespace {
+
+constexpr float kLn2c = 0.6931471805599453f;
+
+__device__ __forceinline__ unsigned short to_bf16(float x) {
+  return __builtin_bit_cast(unsigned short, (__bf16)x);  // round to nearest even
+}
+
+__global__ __launch_bounds__(256) void combine_partials(Problem p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t R = (int64_t)p.B * p.Hq * p.Tq;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int S = p.kv_splits, dv = p.dv;
+  const float* po = p.part;
+  const float* ps = p.part + (int64_t)S * R * dv;
+
+  float M = -INFINITY, x = -INFINITY;
+  for (int s = 0; s < S; ++s) {
+    const float* st = ps + ((int64_t)s * R + r) * 4;
+    x = fmaxf(x, st[1]);
+    M = fmaxf(M, st[2]);
+  }
+  float mass = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* st = ps + ((int64_t)s * R + r) * 4;
+    float wgt = 1.f;
+    if (p.variant == kSoftmax) wgt = st[2] == -INFINITY ? 0.f : exp2f(st[2] - M);
+    mass += wgt * st[0];
+    const float* row = po + ((int64_t)s * R + r) * dv;
+    if (lane < dv) o0 += wgt * row[lane];
+    if (lane + 64 < dv) o1 += wgt * row[lane + 64];
+  }
+  float inv;
+  if (is_yat(p.variant)) inv = 1.f / (mass + 1e-9f);
+  else if (p.variant == kSoftmax) inv = 1.f / mass;
+  else inv = mass > 0.f ? 1.f / mass : 0.f;
+
+  const int64_t i = r % p.Tq, bh = r / p.Tq;
+  const int64_t h = bh % p.Hq, b = bh / p.Hq;
+  unsigned short* orow =
+      (unsigned short*)p.out + b * p.os[0] + h * p.os[1] + i * p.os[2];
+  if (lane < dv) orow[lane] = to_bf16(o0 * inv);
+  if (lane + 64 < dv) orow[lane + 64] = to_bf16(o1 * inv);
+  if (lane == 0) {
+    // softmax: mass relative to the row maximum, max_score in natural units
+    if (p.mass) p.mass[r] = p.variant == kSoftmax ? mass * exp2f(M - x) : mass;
+    if (p.max_score) p.max_score[r] = p.variant == kSoftmax ? x * kLn2c : x;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Problem& p, hipStream_t stream) {
+  const int64_t R = (int64_t)p.B * p.Hq * p.Tq;
+  hipLaunchKernelGGL(combine_partials, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sfs

@@ -30,6 +30,46 @@ __device__ __forceinline__ float yat_numerator(float u, int m) {
 // T_k rounded up to 64, so a 64-key tile never reads past its slice.
 __host__ __device__ inline int64_t nk_pitch(int64_t Tk) { return (Tk + 63) / 64 * 64; }
 
+// Work layout of the bf16 path, chosen on the host so that the workspace size
+// and the launch agree.  rows: query rows per workgroup (256: ping-pong
+// kernel; 128, 64: small-grid kernels).  splits: the keys of each workgroup
+// are cut into this many chunks of whole tiles (small-grid kernels only);
+// each chunk writes unnormalised partials that a combine kernel merges.
+constexpr int kDeviceCUs = 256;
+constexpr int kMaxKvSplits = 64;
+struct Plan {
+  int rows;
+  int splits;
+};
+inline Plan make_plan(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int causal, int block_rows,
+                      int kv_splits) {
+  const int64_t bh = B * Hq;
+  const int64_t n256 = (Tq + 255) / 256 * bh, n128 = (Tq + 127) / 128 * bh,
+                n64 = (Tq + 63) / 64 * bh;
+  Plan pl{block_rows, kv_splits > 0 ? kv_splits : 1};
+  if (pl.rows == 0) {
+    // 256-row workgroups when there are enough of them to fill the device
+    // (with a causal mask, also to balance tiles of unequal length);
+    // otherwise 128- or 64-row workgroups, several per CU.
+    if (kv_splits <= 1 && n256 >= (causal ? 4 : 1) * kDeviceCUs) pl.rows = 256;
+    else pl.rows = n128 >= kDeviceCUs ? 128 : 64;
+  }
+  if (kv_splits == 0 && pl.rows != 256) {
+    // too few waves for the device (2 per SIMD) and long key ranges: split
+    // the keys.  A workgroup of `rows` query rows has rows / 32 waves.
+    const int64_t n_wg = pl.rows == 128 ? n128 : n64;
+    const int64_t want = 8 * kDeviceCUs / (pl.rows / 32);  // workgroups that fill the device
+    const int64_t tiles = (Tk + (pl.rows == 128 ? 63 : 31)) / (pl.rows == 128 ? 64 : 32);
+    if (n_wg < want && tiles >= 8) {
+      int64_t s = (want + n_wg - 1) / n_wg;
+      s = s < tiles / 4 ? s : tiles / 4;  // at least 4 tiles per chunk
+      s = s < kMaxKvSplits ? s : kMaxKvSplits;
+      pl.splits = s > 1 ? (int)s : 1;
+    }
+  }
+  return pl;
+}
+
 // Everything a launch needs, already validated by the ABI layer.  Offsets
 // inside one (batch, head) slice fit in int32 (checked there); the per-slice
 // base offsets are 64-bit.
@@ -48,10 +88,16 @@ struct Problem {
   int B, Hq, Hkv, Tq, Tk, dk, dv;
   int variant;
   int causal;
-  int block_rows;     // 0: choose by grid size; 64, 128, 256: force that kernel
+  int block_rows;     // query rows per workgroup: 64, 128 or 256 (bf16; planned)
+  int kv_splits;      // key chunks per workgroup (>= 1); > 1 writes partials
+  float* part;        // kv_splits > 1: partial O [S][R][dv] then stats [S][R][4]
+                      // (mass, max, reference max), R = B*Hq*Tq
   int yat_power;      // Yat numerator power m >= 1 ((s + b)^(2m))
   int yat_bias_free;  // Yat: b = 0 exactly (b_raw not read)
 };
+
+// Merges the kv_splits partials of every row into out, mass and max_score.
+hipError_t launch_combine(const Problem& p, hipStream_t stream);
 
 // Fused forward for fp32 storage (vector-ALU path).
 hipError_t launch_f32(const Problem& p, hipStream_t stream);

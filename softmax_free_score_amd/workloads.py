@@ -5,7 +5,7 @@ the storage dtype -- nothing of the method's arithmetic.  The tests, the
 benchmark and the oracle-side checks all take their inputs from here, so both
 sides of a parity check see the same bytes.
 
-The five workloads stand in for the pages' models (a character-level GPT with
+The six workloads stand in for the pages' models (a character-level GPT with
 6 layers, 4 heads, width 192 and context 128 in "The Kernel Between the
 Roles", "The run"; Qwen3-1.7B-class GQA attention for the s^tau post; the
 cross-attention shapes T_q != T_k, d_v != d_k of "NNX Scaled Dot-Product
@@ -22,6 +22,9 @@ stau_gqa   B=2, Hq=16, Hkv=8, T=2048, d=128, bf16, causal; q,k,v ~ N(0,1);
            log_tau ~ U(-1,2); seed 3
 cross      B=8, H=8, Tq=1024, Tk=8192, dk=64, dv=128, bf16, non-causal;
            q,k ~ N(0,1); v ~ U(-1,1); seed 4
+decode     B=8, Hq=16, Hkv=8, Tq=1, Tk=8192, d=128, bf16, non-causal: one new
+           query row per head against a long key cache (the Qwen3-1.7B-class
+           head layout of the s^tau post, at inference); q,k,v ~ N(0,1); seed 5
 =========  ====================================================================
 
 Draw order is fixed: q, k, v, b_raw, eps_raw, log_tau, each as fp32 from
@@ -86,6 +89,9 @@ WORKLOADS = {
     "cross": Workload("cross", 8, 8, 8, 1024, 8192, 64, 128, "bf16", False, 4, 1.0,
                       "uniform", ("uniform", -1.0, 1.0), ("uniform", -3.0, 0.0),
                       ("softmax", "yat", "stau")),
+    "decode": Workload("decode", 8, 16, 8, 1, 8192, 128, 128, "bf16", False, 5, 1.0,
+                       "normal", ("uniform", -1.0, 1.0), ("uniform", -3.0, 0.0),
+                       ("yat", "softmax", "stau")),
 }
 
 

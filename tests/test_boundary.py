@@ -160,3 +160,37 @@ def test_yat_options_validation(opts, b, status):
 def test_yat_options_need_eps_and_desc():
     assert call_yat(desc(), attn.AttnYatOpts(1, 1), e=0) == ERR_PARAM
     assert call_yat(None, None) == ERR_NULL
+
+
+@pytest.mark.parametrize("splits,dtype,rows,reserved,status", [
+    (-1, attn.ATTN_BF16, 0, 0, ERR_UNSUP),
+    (65, attn.ATTN_BF16, 0, 0, ERR_UNSUP),
+    (2, attn.ATTN_F32, 0, 0, ERR_UNSUP),          # splitting is a bf16-path feature
+    (2, attn.ATTN_BF16, 256, 0, ERR_UNSUP),       # not with the 256-row kernel
+    (0, attn.ATTN_BF16, 0, 1, ERR_UNSUP),         # reserved must be 0
+    (2, attn.ATTN_BF16, 64, 0, ERR_HIP),          # valid: fails only for want of a device
+    (64, attn.ATTN_BF16, 128, 0, ERR_HIP),
+    (1, attn.ATTN_F32, 0, 0, ERR_HIP)])
+def test_kv_splits_validation(splits, dtype, rows, reserved, status):
+    d = desc(dtype=dtype)
+    assert d.kv_splits == 0 and d.reserved == 0     # attn_desc_init: library's choice
+    d.kv_splits, d.block_rows, d.reserved = splits, rows, reserved
+    assert call(d, ws_bytes=1 << 30) == status
+
+
+def ws(d, variant):
+    return attn.load_library().attn_fwd_workspace_bytes(ctypes.byref(d), variant)
+
+
+def test_workspace_bytes_with_splits():
+    # decode-like: 1 query row against 4096 keys -> the plan splits the keys
+    d = desc(B=2, Hq=8, Hkv=2, Tq=1, Tk=4096, dk=128, dv=128)
+    assert ws(d, attn.ATTN_SOFTMAX) > 0
+    d.kv_splits = 1                                   # no split: softmax needs nothing
+    assert ws(d, attn.ATTN_SOFTMAX) == 0
+    d.kv_splits = 3                                   # 3 chunks x 16 rows x (128 + 4) floats
+    assert ws(d, attn.ATTN_SOFTMAX) == 3 * 16 * 132 * 4
+    nk = 2 * 2 * 4096 * 4                             # Yat: |k|^2 rows first (256-aligned)
+    assert ws(d, attn.ATTN_YAT) == nk + 3 * 16 * 132 * 4
+    d.dtype = attn.ATTN_F32
+    assert ws(d, attn.ATTN_SOFTMAX) == 0

@@ -25,7 +25,7 @@ def v_max(inp):
 BLOCK_ROWS = (0, 64, 128, 256)
 
 
-def full_check(inp, variant, causal, label, block_rows=(0,), yat_opts=None):
+def full_check(inp, variant, causal, label, block_rows=(0,), yat_opts=None, kv_splits=0):
     say(f"[gpu] {label} {variant} causal={causal} shape B{inp.wl.B} Hq{inp.wl.Hq} "
         f"Hkv{inp.wl.Hkv} Tq{inp.wl.Tq} Tk{inp.wl.Tk} dk{inp.wl.dk} dv{inp.wl.dv} {inp.wl.dtype}"
         f"{'' if yat_opts is None else f' yat_opts={yat_opts}'}")
@@ -33,7 +33,7 @@ def full_check(inp, variant, causal, label, block_rows=(0,), yat_opts=None):
     ref = oracle_full(inp, variant, causal, yat_opts)
     for rows in block_rows:
         got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal, yat_opts=yat_opts,
-                                         block_rows=rows)]
+                                         block_rows=rows, kv_splits=kv_splits)]
         check(inp.wl.dtype, got, ref, v_max(inp), f"{label}/{variant}/rows{rows}",
               v_rms=v_rms(inp))
 
@@ -147,6 +147,57 @@ def test_yat_default_options_match_attn_fwd():
         assert torch.equal(x, y)
 
 
+# ------------------------------------- key splits (partials + combine)
+
+SPLITS = [(64, 2), (64, 5), (128, 3), (0, 0)]   # (block_rows, kv_splits); (0, 0): library's plan
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", [MEDIUM[0], MEDIUM[1], MEDIUM[2], MEDIUM[6],
+                                   (1, 4, 2, 64, 1500, 128, 128, False)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_kv_splits_bf16(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=19, qk_std=1.5)
+    say(f"[gpu] kv splits {variant} {shape}")
+    q, k, v, prm = to_device(inp)
+    ref = oracle_full(inp, variant, causal)
+    for rows, splits in SPLITS:
+        got = [to_np(t) for t in run_gpu(q, k, v, prm, variant, causal, block_rows=rows,
+                                         kv_splits=splits)]
+        check("bf16", got, ref, v_max(inp), f"splits/{variant}/rows{rows}/s{splits}",
+              v_rms=v_rms(inp))
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 1, 3000, 128, 128), (4, 16, 8, 4, 2049, 64, 64),
+                                   (1, 2, 1, 7, 9000, 128, 32)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_decode_shapes(variant, shape):
+    # few query rows against long keys: the library splits the keys by itself
+    B, Hq, Hkv, Tq, Tk, dk, dv = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", False, seed=20, qk_std=1.0)
+    full_check(inp, variant, False, "decode")
+
+
+def test_kv_splits_more_chunks_than_tiles():
+    # 64 chunks over 4 tiles of keys: most chunks are empty and write neutral partials
+    inp = make_custom(1, 2, 2, 40, 100, 64, 64, "bf16", False, seed=21)
+    for variant in ("yat", "softmax", "stau"):
+        full_check(inp, variant, False, "splits64", block_rows=(64,), kv_splits=64)
+
+
+def test_kv_splits_with_yat_options_and_determinism():
+    inp = make_custom(1, 4, 2, 96, 2000, 128, 128, "bf16", False, seed=22, qk_std=1.0)
+    full_check(inp, "yat", False, "splits_yat_opts", block_rows=(64, 128), yat_opts=(2, True),
+               kv_splits=4)
+    q, k, v, prm = to_device(inp)
+    a = run_gpu(q, k, v, prm, "softmax", False, kv_splits=6)
+    b = run_gpu(q, k, v, prm, "softmax", False, kv_splits=6)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # --------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
@@ -249,7 +300,8 @@ def test_unit_values_give_weight_sums(variant):
 
 FULL = [("long_yat", "yat", False), ("long_yat", "softmax", False), ("long_yat", "yat", True),
         ("stau_gqa", "stau", False), ("cross", "softmax", False), ("cross", "yat", False),
-        ("cross", "stau", False), ("gpt_small", "yat", True)]
+        ("cross", "stau", False), ("gpt_small", "yat", True), ("decode", "yat", False),
+        ("decode", "softmax", False), ("decode", "stau", False)]
 
 
 @pytest.mark.parametrize("name,variant,tied", FULL, ids=lambda x: str(x))
