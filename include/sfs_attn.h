@@ -176,6 +176,34 @@ int attn_fwd_yat(const attn_desc* desc, const void* q, const void* k, const void
                  int causal, void* out, float* mass, float* max_score, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Attention telemetry: one extra pass over the score tiles of a finished
+ * forward (same desc, q, k, variant, per-head parameters and mask), given the
+ * row statistics that forward returned.  The weights of every allowed pair are
+ * recomputed as the forward defines them, and the pass returns:
+ *   row_entropy   [B,Hq,Tq]: -sum_j w_ij ln w_ij / ln(n_i) over the n_i allowed
+ *                 keys, 0 when n_i = 1 ("The Kernel Between the Roles", "What
+ *                 each normalizer forgets": 0 for a row on one key, 1 for
+ *                 uniform weights);
+ *   row_sparsity  [B,Hq,Tq]: the fraction of allowed keys with w_ij below
+ *                 sparsity_threshold (the s^tau post measures weights < 1e-6);
+ *   tau_star      [Hq]: Cov(s, ln phi(s)) / Var(ln phi(s)) over all allowed
+ *                 pairs of query head h, s = q.k / sqrt(d_k), phi = softplus(s)
+ *                 + 1e-6 (the s^tau post's closed form for the tau at which
+ *                 s^tau is closest to softmax; NaN when Var = 0).
+ * Inputs: mass (all maps) and max_score (softmax) as the forward wrote them,
+ * fp32 [B,Hq,Tq], contiguous.  Outputs are device fp32 and may be NULL (not
+ * computed); at least one must be given.  v is not read (desc's v fields must
+ * still describe a valid tensor shape).  bf16 storage and the standard maps
+ * only (the Yat options of attn_fwd_yat are not covered).  Workspace:
+ * attn_telemetry_workspace_bytes(desc, variant).  Errors as attn_fwd;
+ * sparsity_threshold must be > 0 (else ATTN_ERR_PARAM). */
+size_t attn_telemetry_workspace_bytes(const attn_desc* desc, int variant);
+int attn_telemetry(const attn_desc* desc, const void* q, const void* k, int variant,
+                   const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
+                   const float* mass, const float* max_score, float sparsity_threshold,
+                   float* row_entropy, float* row_sparsity, float* tau_star, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

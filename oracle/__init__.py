@@ -191,3 +191,56 @@ def attn_fwd_np(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal
     else:
         raise ValueError(f"unknown variant {variant}")
     return w @ vh, mass, max_score
+
+
+def telemetry_np(q, k, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False,
+                 sparsity_threshold=1e-6):
+    """Attention telemetry, fp64 (numpy).  Returns (row_entropy, row_sparsity,
+    tau_star): row_entropy and row_sparsity [B,Hq,Tq], tau_star [Hq].
+
+    * row_entropy: the entropy of the row's weights over its allowed keys,
+      -sum w ln w, divided by ln(n) for n allowed keys (0 for n = 1): 0 for a
+      row that puts everything on one key, 1 for uniform weights ("The Kernel
+      Between the Roles", "What each normalizer forgets").
+    * row_sparsity: the fraction of allowed keys whose weight is below the
+      threshold (the s^tau post's sparsity, weights < 1e-6).
+    * tau_star: per query head, Cov(s, ln phi(s)) / Var(ln phi(s)) over every
+      allowed (query, key) pair of the head, s = q.k / sqrt(d_k),
+      phi = softplus(s) + 1e-6 (the s^tau post's closed form for the tau that
+      makes s^tau closest to softmax); NaN when Var = 0.
+
+    The weights are those of the forward for ``variant`` (Yat: kappa /
+    (mass + 1e-9); softmax; s^tau), computed here from q and k."""
+    variant = VARIANTS.get(variant, variant)
+    q, k = (np.asarray(a, dtype=np.float64) for a in (q, k))
+    B, Hq, Tq, dk = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    kh = np.repeat(k, g, axis=1)
+    dots = q @ np.swapaxes(kh, -1, -2)
+    allowed = np.tril(np.ones((Tq, Tk), bool)) if causal else np.ones((Tq, Tk), bool)
+    allowed = np.broadcast_to(allowed, dots.shape)
+    eye = np.eye(Tk)
+    if variant == YAT:
+        # the forward's weights, read off with V = identity
+        w = attn_fwd_np(q, k, np.broadcast_to(eye, (B, Hkv, Tk, Tk)), YAT, b_raw, eps_raw,
+                        causal=causal)[0]
+    else:
+        w = attn_fwd_np(q, k, np.broadcast_to(eye, (B, Hkv, Tk, Tk)), variant, b_raw, eps_raw,
+                        log_tau, causal=causal)[0]
+    n = allowed.sum(-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        wlnw = np.where(allowed & (w > 0), w * np.log(np.where(w > 0, w, 1.0)), 0.0)
+    ent = -wlnw.sum(-1)
+    row_entropy = np.where(n > 1, ent / np.log(np.maximum(n, 2)), 0.0)
+    row_sparsity = np.where(allowed, w < sparsity_threshold, False).sum(-1) / n
+    s = dots / np.sqrt(dk)
+    L = np.log(softplus(s) + 1e-6)
+    tau = np.empty(Hq)
+    for h in range(Hq):
+        m = allowed[:, h]
+        sv, lv = s[:, h][m], L[:, h][m]
+        cov = np.mean(sv * lv) - np.mean(sv) * np.mean(lv)
+        var = np.mean(lv * lv) - np.mean(lv) ** 2
+        tau[h] = cov / var if var > 0 else np.nan
+    return row_entropy, row_sparsity, tau

@@ -28,7 +28,8 @@ VARIANTS = {"softmax": ATTN_SOFTMAX, "yat": ATTN_YAT, "stau": ATTN_STAU}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
           -4: "ATTN_ERR_PARAM", -5: "ATTN_ERR_WORKSPACE", -6: "ATTN_ERR_HIP"}
 EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_yat",
-           "attn_status_string", "attn_last_error")
+           "attn_telemetry_workspace_bytes", "attn_telemetry", "attn_status_string",
+           "attn_last_error")
 ATTN_YAT_MAX_POWER = 8
 
 
@@ -79,6 +80,12 @@ def load_library():
                                      ctypes.POINTER(AttnYatOpts), ctypes.c_int, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
         lib.attn_fwd_yat.restype = ctypes.c_int
+        lib.attn_telemetry_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+        lib.attn_telemetry_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_telemetry.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, ctypes.c_int, vp, vp,
+                                       vp, ctypes.c_int, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
+        lib.attn_telemetry.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -218,3 +225,34 @@ def call_raw_yat(desc: AttnDesc, q, k, v, b_raw, eps_raw, opts, causal, out, mas
     return int(lib.attn_fwd_yat(dp, p(q), p(k), p(v), p(b_raw), p(eps_raw), op, int(causal),
                                 p(out), p(mass), p(max_score), p(workspace),
                                 int(workspace_bytes), p(stream)))
+
+
+def attn_telemetry(q, k, variant, mass, max_score=None, b_raw=None, eps_raw=None, log_tau=None,
+                   causal=False, sparsity_threshold=1e-6, entropy=True, sparsity=True,
+                   tau_star=True, workspace=None, stream=None):
+    """One telemetry pass after a forward with the same inputs: returns
+    (row_entropy [B,Hq,Tq], row_sparsity [B,Hq,Tq], tau_star [Hq]) as float32
+    device tensors (None for the ones not asked for).  ``mass`` and
+    ``max_score`` are the forward's outputs."""
+    lib = load_library()
+    variant = VARIANTS.get(variant, variant)
+    B, Hq, Tq, _ = q.shape
+    desc = make_desc(q, k, k, q)   # v and out are not used; k and q give valid shapes
+    f32 = dict(dtype=torch.float32, device=q.device)
+    ent = torch.empty((B, Hq, Tq), **f32) if entropy else None
+    spa = torch.empty((B, Hq, Tq), **f32) if sparsity else None
+    tau = torch.empty((Hq,), **f32) if tau_star else None
+    need = int(lib.attn_telemetry_workspace_bytes(ctypes.byref(desc), variant))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    st = lib.attn_telemetry(ctypes.byref(desc), _ptr(q), _ptr(k), variant, _ptr(b_raw),
+                            _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(mass),
+                            _ptr(max_score), float(sparsity_threshold), _ptr(ent), _ptr(spa),
+                            _ptr(tau), _ptr(workspace), ws_bytes,
+                            ctypes.c_void_p(stream) if stream else None)
+    if st != 0:
+        raise AttnError(st, lib.attn_last_error().decode())
+    return ent, spa, tau

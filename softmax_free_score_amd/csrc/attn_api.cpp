@@ -64,7 +64,7 @@ size_t ws_need(const attn_desc* d, int variant) {
 int validate(const attn_desc* d, const void* q, const void* k, const void* v, int variant,
              const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
              const void* out, const float* mass, const float* max_score, const void* ws,
-             size_t ws_bytes, bool yat_bias_free, bool* empty) {
+             size_t ws_bytes, bool yat_bias_free, bool* empty, int64_t ws_need = -1) {
   *empty = false;
   if (!d) {
     set_error("desc is NULL");
@@ -138,7 +138,7 @@ int validate(const attn_desc* d, const void* q, const void* k, const void* v, in
               "and one (batch, head) slice must span less than 2^31 bytes");
     return ATTN_ERR_UNSUPPORTED;
   }
-  const size_t need = attn_fwd_workspace_bytes(d, variant);
+  const size_t need = ws_need >= 0 ? (size_t)ws_need : attn_fwd_workspace_bytes(d, variant);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) {
     set_error("workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()");
     return ATTN_ERR_WORKSPACE;
@@ -256,6 +256,84 @@ int attn_fwd_yat(const attn_desc* d, const void* q, const void* k, const void* v
   }
   return run(d, q, k, v, ATTN_YAT, b_raw, eps_raw, nullptr, power, bias_free, causal, out, mass,
              max_score, workspace, workspace_bytes, stream);
+}
+
+size_t attn_telemetry_workspace_bytes(const attn_desc* d, int variant) {
+  if (!d || d->dtype != ATTN_BF16) return 0;
+  if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0) return 0;
+  const size_t nk = variant == ATTN_YAT ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
+  const size_t n_qt = (size_t)((d->Tq + sfs::kStatsRows - 1) / sfs::kStatsRows);
+  return (nk + 255) / 256 * 256 + (size_t)(d->Hq * d->B) * n_qt * 8 * sizeof(double);
+}
+
+int attn_telemetry(const attn_desc* d, const void* q, const void* k, int variant,
+                   const float* b_raw, const float* eps_raw, const float* log_tau, int causal,
+                   const float* mass, const float* max_score, float sparsity_threshold,
+                   float* row_entropy, float* row_sparsity, float* tau_star, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (d && d->dtype != ATTN_BF16) {
+    set_error("telemetry is built for bf16 storage");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (!mass || (variant == ATTN_SOFTMAX && !max_score) ||
+      (!row_entropy && !row_sparsity && !tau_star)) {
+    set_error("telemetry needs the forward's mass (and max_score for softmax) and an output");
+    return ATTN_ERR_NULL;
+  }
+  if (!(sparsity_threshold > 0.f)) {
+    set_error("sparsity_threshold must be > 0");
+    return ATTN_ERR_PARAM;
+  }
+  for (const float* t : {row_entropy, row_sparsity, tau_star})
+    if (reinterpret_cast<uintptr_t>(t) & 3u) {
+      set_error("telemetry outputs must be 4-byte aligned");
+      return ATTN_ERR_UNSUPPORTED;
+    }
+  bool empty = false;
+  // v and out are not used: k stands in for their pointer checks
+  const int st = validate(d, q, k, k, variant, b_raw, eps_raw, log_tau, causal, k, mass,
+                          max_score, workspace, workspace_bytes, false, &empty,
+                          (int64_t)attn_telemetry_workspace_bytes(d, variant));
+  if (st != ATTN_OK || empty) return st;
+
+  sfs::Problem p{};
+  p.q = q; p.k = k;
+  p.b_raw = b_raw; p.eps_raw = eps_raw; p.log_tau = log_tau;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = d->q_stride[i]; p.ks[i] = d->k_stride[i];
+  }
+  p.B = (int)d->B; p.Hq = (int)d->Hq; p.Hkv = (int)d->Hkv;
+  p.Tq = (int)d->Tq; p.Tk = (int)d->Tk; p.dk = (int)d->dk; p.dv = (int)d->dv;
+  p.variant = variant;
+  p.causal = causal ? 1 : 0;
+  p.yat_power = 1;
+  p.in_mass = mass; p.in_max = max_score;
+  p.sparsity_threshold = sparsity_threshold;
+  p.row_entropy = row_entropy; p.row_sparsity = row_sparsity; p.tau_star = tau_star;
+  const size_t nk = variant == ATTN_YAT ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
+  p.nk = static_cast<float*>(workspace);
+  if (tau_star)
+    p.tau_part = reinterpret_cast<double*>(static_cast<char*>(workspace) + (nk + 255) / 256 * 256);
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (p.dk) {
+      case 16: e = sfs::launch_stats_bf16_dk16(p, s); break;
+      case 32: e = sfs::launch_stats_bf16_dk32(p, s); break;
+      case 64: e = sfs::launch_stats_bf16_dk64(p, s); break;
+      default: e = sfs::launch_stats_bf16_dk128(p, s); break;
+    }
+    if (e == hipSuccess && tau_star) e = sfs::launch_tau_star(p, s);
+  }
+  if (e != hipSuccess) {
+    char msg[256];
+    std::snprintf(msg, sizeof msg, "HIP: %s (%s)", hipGetErrorName(e), hipGetErrorString(e));
+    set_error(msg);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
 }
 
 const char* attn_status_string(int status) {

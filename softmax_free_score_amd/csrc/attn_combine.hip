@@ -70,7 +70,30 @@ __global__ __launch_bounds__(256) void combine_partials(Problem p) {
   }
 }
 
+// tau* of query head h = blockIdx.x * 64 + lane from the per-(head, batch,
+// query tile) sums of the telemetry pass, in a fixed order (the s^tau post:
+// tau* = Cov(s, ln phi(s)) / Var(ln phi(s))).  NaN when Var = 0.
+__global__ __launch_bounds__(64) void tau_star_kernel(Problem p, int n_qt) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= p.Hq) return;
+  double a[6] = {0, 0, 0, 0, 0, 0};
+  const double* src = p.tau_part + (int64_t)h * p.B * n_qt * 8;
+  for (int64_t i = 0; i < (int64_t)p.B * n_qt; ++i)
+    for (int j = 0; j < 6; ++j) a[j] += src[i * 8 + j];
+  const double n = a[0];
+  const double ms = a[1] / n, ml = a[2] / n;
+  const double cov = a[5] / n - ms * ml;
+  const double var = a[4] / n - ml * ml;
+  p.tau_star[h] = var > 0.0 ? (float)(cov / var) : __builtin_nanf("");
+}
+
 }  // namespace
+
+hipError_t launch_tau_star(const Problem& p, hipStream_t stream) {
+  const int n_qt = (p.Tq + kStatsRows - 1) / kStatsRows;
+  hipLaunchKernelGGL(tau_star_kernel, dim3((p.Hq + 63) / 64), dim3(64), 0, stream, p, n_qt);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const Problem& p, hipStream_t stream) {
   const int64_t R = (int64_t)p.B * p.Hq * p.Tq;

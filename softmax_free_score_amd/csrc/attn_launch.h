@@ -92,9 +92,28 @@ struct Problem {
   int kv_splits;      // key chunks per workgroup (>= 1); > 1 writes partials
   float* part;        // kv_splits > 1: partial O [S][R][dv] then stats [S][R][4]
                       // (mass, max, reference max), R = B*Hq*Tq
+  // telemetry pass (attn_telemetry): the forward's row statistics in, row
+  // entropy / sparsity out, per-(head, batch, query tile) tau sums
+  const float* in_mass;
+  const float* in_max;
+  float sparsity_threshold;
+  float* row_entropy;
+  float* row_sparsity;
+  double* tau_part;   // [Hq][B][n_qt][8]: count, sum s, sum L, sum s^2, sum L^2, sum sL
+  float* tau_star;
   int yat_power;      // Yat numerator power m >= 1 ((s + b)^(2m))
   int yat_bias_free;  // Yat: b = 0 exactly (b_raw not read)
 };
+
+// Telemetry pass: per-row entropy and sparsity of the weights, tau sums.
+hipError_t launch_stats_bf16_dk16(const Problem& p, hipStream_t stream);
+hipError_t launch_stats_bf16_dk32(const Problem& p, hipStream_t stream);
+hipError_t launch_stats_bf16_dk64(const Problem& p, hipStream_t stream);
+hipError_t launch_stats_bf16_dk128(const Problem& p, hipStream_t stream);
+// tau* per query head from the tau sums (fixed summation order).
+hipError_t launch_tau_star(const Problem& p, hipStream_t stream);
+// Query rows per workgroup of the telemetry pass.
+constexpr int kStatsRows = 64;
 
 // Merges the kv_splits partials of every row into out, mass and max_score.
 hipError_t launch_combine(const Problem& p, hipStream_t stream);

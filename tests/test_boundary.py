@@ -194,3 +194,35 @@ def test_workspace_bytes_with_splits():
     assert ws(d, attn.ATTN_YAT) == nk + 3 * 16 * 132 * 4
     d.dtype = attn.ATTN_F32
     assert ws(d, attn.ATTN_SOFTMAX) == 0
+
+
+def call_tel(d, variant=attn.ATTN_SOFTMAX, mass=M, mx=X, thr=1e-6, ent=O, spa=O + 0x100,
+             tau=O + 0x200, b=BR, e=ER, lt=LT):
+    lib = attn.load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.attn_telemetry(ctypes.byref(d) if d is not None else None, p(A), p(K), variant,
+                              p(b), p(e), p(lt), 1, p(mass), p(mx), ctypes.c_float(thr), p(ent),
+                              p(spa), p(tau), p(W), 1 << 30, None)
+
+
+def test_telemetry_validation():
+    assert call_tel(desc()) == ERR_HIP                               # valid, no device
+    assert call_tel(desc(dtype=attn.ATTN_F32)) == ERR_UNSUP
+    assert call_tel(desc(), mass=0) == ERR_NULL
+    assert call_tel(desc(), mx=0) == ERR_NULL                        # softmax needs max_score
+    assert call_tel(desc(), variant=attn.ATTN_YAT, mx=0) == ERR_HIP  # Yat does not
+    assert call_tel(desc(), ent=0, spa=0, tau=0) == ERR_NULL
+    assert call_tel(desc(), thr=0.0) == ERR_PARAM
+    assert call_tel(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
+    assert call_tel(None) == ERR_NULL
+
+
+def test_telemetry_workspace_bytes():
+    lib = attn.load_library()
+    d = desc(B=2, Hq=4, Hkv=2, Tq=130, Tk=100, dk=64, dv=64)
+    n_qt = 3                                                          # 130 rows / 64
+    tau_bytes = 4 * 2 * n_qt * 8 * 8
+    assert lib.attn_telemetry_workspace_bytes(ctypes.byref(d), attn.ATTN_SOFTMAX) == tau_bytes
+    nk = 2 * 2 * 128 * 4                                              # |k|^2 rows, pitch 128
+    assert lib.attn_telemetry_workspace_bytes(ctypes.byref(d), attn.ATTN_YAT) == \
+        (nk + 255) // 256 * 256 + tau_bytes

@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from parity import (check, oracle_full, oracle_rows, run_gpu, sample_rows, say, to_device,
                     to_np)
 from softmax_free_score_amd.workloads import WORKLOADS, make_custom, make_inputs
@@ -196,6 +198,66 @@ def test_kv_splits_with_yat_options_and_determinism():
     b = run_gpu(q, k, v, prm, "softmax", False, kv_splits=6)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ------------------------------------------------- telemetry (attn_telemetry)
+
+# Tolerances: the pass recomputes each weight in fp32 from the same bf16
+# inputs and the forward's fp32 row normaliser, so weights carry ~1e-5
+# relative error: entropy |d| <= 2e-3; sparsity may differ by weights that sit
+# at the threshold: |d| <= 2 / n + 1e-3; tau* (fp32 per-lane sums, fp64 above)
+# |d| <= 2e-3 |ref|.
+TEL_SHAPES = [(2, 4, 2, 200, 200, 64, 64, True), (1, 2, 1, 70, 300, 128, 128, False),
+              (1, 4, 4, 97, 97, 16, 16, True), (1, 2, 2, 130, 130, 32, 32, False)]
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", TEL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_telemetry_parity(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=24, qk_std=2.0)
+    say(f"[gpu] telemetry {variant} {shape}")
+    q, k, v, prm = to_device(inp)
+    _, mass, mx = run_gpu(q, k, v, prm, variant, causal)
+    from softmax_free_score_amd import attn
+    ent, spa, tau = attn.attn_telemetry(q, k, variant, mass, mx, causal=causal, **prm)
+    torch.cuda.synchronize()
+    qq, kk, _ = inp.f64()
+    r_ent, r_spa, r_tau = oracle.telemetry_np(
+        qq, kk, variant, causal=causal, **{n: a.astype(np.float64) for n, a in inp.params().items()})
+    n = (np.arange(Tq)[:, None] >= np.arange(Tk)[None, :]).sum(1) if causal else np.full(Tq, Tk)
+    assert np.abs(to_np(ent) - r_ent).max() <= 2e-3
+    assert np.all(np.abs(to_np(spa) - r_spa) <= 2.0 / n + 1e-3)
+    assert np.all(np.abs(to_np(tau) - r_tau) <= 2e-3 * np.abs(r_tau))
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax"])
+def test_telemetry_full_size_properties(variant):
+    wl = WORKLOADS["long_yat"]
+    inp = make_inputs(wl)
+    say(f"[gpu] telemetry full-size long_yat {variant}")
+    q, k, v, prm = to_device(inp)
+    _, mass, mx = run_gpu(q, k, v, prm, variant, True)
+    from softmax_free_score_amd import attn
+    ent, spa, tau = attn.attn_telemetry(q, k, variant, mass, mx, causal=True, **prm)
+    torch.cuda.synchronize()
+    assert torch.all((ent >= 0) & (ent <= 1 + 1e-5)) and torch.all((spa >= 0) & (spa <= 1))
+    assert torch.all(torch.isfinite(tau))
+    # row 0 of every head sees one key: entropy 0, sparsity 0
+    assert torch.all(ent[:, :, 0] == 0) and torch.all(spa[:, :, 0] == 0)
+
+
+def test_telemetry_outputs_are_optional_and_sparsity_threshold():
+    inp = make_custom(1, 2, 2, 64, 64, 64, 64, "bf16", False, seed=25, qk_std=3.0)
+    q, k, v, prm = to_device(inp)
+    _, mass, mx = run_gpu(q, k, v, prm, "softmax", False)
+    from softmax_free_score_amd import attn
+    e1, s1, t1 = attn.attn_telemetry(q, k, "softmax", mass, mx, **prm)
+    e2, s2, t2 = attn.attn_telemetry(q, k, "softmax", mass, mx, entropy=False, tau_star=False,
+                                     sparsity_threshold=1e-30, **prm)
+    torch.cuda.synchronize()
+    assert e2 is None and t2 is None and torch.all(s2 <= s1)
+    assert float(s1.mean()) > 0.0     # qk_std 3: many weights below 1e-6
 
 
 # --------------------------------------------------------------- edge cases

@@ -477,3 +477,63 @@ def test_oracle_rejects_bad_arguments():
         oracle.attn_fwd_c(q, k, v, "softmax", rows=[3])
     with pytest.raises(ValueError):      # Yat numerator power below 1
         oracle.attn_fwd_c(q, k, v, "yat", b_raw=np.zeros(1), eps_raw=np.zeros(1), yat_power=0)
+
+
+# --------------------------------------------------------------------------
+# Telemetry: normalised row entropy ("The Kernel Between the Roles", "What
+# each normalizer forgets"), sparsity and tau* (the s^tau post)
+
+def tel(q, k, variant, causal=False, **kw):
+    q, k = np.asarray(q, float)[None, None], np.asarray(k, float)[None, None]
+    prm = dict(b_raw=np.zeros(1), eps_raw=np.zeros(1), log_tau=np.zeros(1))
+    prm.update(kw)
+    e, s, t = oracle.telemetry_np(q, k, variant, causal=causal, **prm)
+    return e[0, 0], s[0, 0], t[0]
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_entropy_of_equal_keys_is_one(variant):
+    # identical keys get identical weights: the entropy is ln n, normalised 1
+    e, s, _ = tel([[0.3, -1.2], [2.0, 0.5]], [[1.0, 0.4]] * 5, variant)
+    # (Yat weights sum to mass / (mass + 1e-9), which moves the entropy by ~1e-9)
+    np.testing.assert_allclose(e, 1.0, rtol=0, atol=1e-8 if variant == "yat" else 1e-12)
+    assert np.all(s == 0.0)
+
+
+def test_entropy_two_keys_is_binary_entropy():
+    # softmax over two logits a, b: p = 1 / (1 + e^(b - a)); H = -p ln p - q ln q
+    a, b = 0.7, -1.9
+    e, _, _ = tel([[1.0]], [[a], [b]], "softmax")
+    p = 1.0 / (1.0 + math.exp(b - a))
+    h = -(p * math.log(p) + (1 - p) * math.log(1 - p)) / math.log(2.0)
+    assert abs(e[0] - h) < 1e-13
+
+
+def test_entropy_one_allowed_key_is_zero():
+    e, s, _ = tel([[1.0], [2.0]], [[0.5], [0.1]], "yat", causal=True)
+    assert e[0] == 0.0 and s[0] == 0.0          # row 0 sees one key
+
+
+def test_sparsity_counts_weights_below_threshold():
+    # logits 0, -20, -20, 0: two weights e^-20 / (2 + 2 e^-20) < 1e-6
+    _, s, _ = tel([[1.0]], [[0.0], [-20.0], [-20.0], [0.0]], "softmax")
+    assert s[0] == 0.5
+    _, s, _ = tel([[1.0]], [[0.0], [-20.0], [-20.0], [0.0]], "softmax", sparsity_threshold=1e-12)
+    assert s[0] == 0.0
+
+
+def test_tau_star_two_score_values_is_the_slope():
+    # with two distinct scores the least-squares slope of s on ln phi(s) runs
+    # through both points: tau* = (s1 - s2) / (ln phi(s1) - ln phi(s2))
+    s1, s2 = 1.5, -0.25
+    _, _, t = tel([[1.0]], [[s1], [s2], [s1]], "stau")
+    lp = lambda s: math.log(max(s, 0.0) + math.log1p(math.exp(-abs(s))) + 1e-6)
+    assert abs(t - (s1 - s2) / (lp(s1) - lp(s2))) < 1e-12
+
+
+def test_tau_star_ignores_masked_pairs_and_is_undefined_without_spread():
+    # causal: row 0 sees only key 0; all allowed scores equal -> Var = 0 -> NaN
+    _, _, t = tel([[1.0], [1.0]], [[0.5], [9.0]], "softmax", causal=True)
+    assert math.isnan(t) is False                # keys 0.5 (x2) and 9.0 differ
+    _, _, t = tel([[1.0], [1.0]], [[0.5], [0.5]], "softmax")
+    assert math.isnan(t)
