@@ -1,4 +1,4 @@
-"""Fp64 CPU oracle for the attention forward -- TEST INFRASTRUCTURE ONLY.
+"""Fp64 CPU oracle for the attention forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never calls it, and
@@ -27,6 +27,12 @@ What each computes, with the pages it follows:
   phi = softplus(s) + 1e-6, tau = softplus(log_tau) + 1 per head,
   w = phi^tau / sum phi^tau over allowed keys, out = w @ v.
 
+* ``attn_bwd_np`` -- gradients of L = sum(dout * out) with respect to q, k, v
+  and the per-head parameters (b_raw, eps_raw, log_tau) of the three maps
+  above: the chain rule through their closed forms, written out in fp64
+  (the pages train these models by automatic differentiation and print no
+  backward formulas; the derivation is in the function's docstring).
+
 Readings of points the pages leave open (GQA mapping h -> h // (Hq/Hkv),
 causal j <= i with Tq == Tk, masked keys weigh exactly 0 in all branches,
 mass and max_score per branch) are those stated in ``attn_oracle.c``.
@@ -36,6 +42,9 @@ Parity status: every function here is pinned by tests in
 forms, invariants and brute force).  The mass and max_score conventions for
 softmax and s^tau and the GQA mapping are conventions of this build, pinned
 only by brute force and self-consistency (parity unpinned by the pages).
+``attn_bwd_np`` is pinned in ``tests/test_oracle_bwd_pins.py`` to central
+finite differences of the C forward, to PyTorch autograd through its own
+scaled dot-product attention (softmax), and to closed forms and invariants.
 """
 from __future__ import annotations
 
@@ -244,3 +253,87 @@ def telemetry_np(q, k, variant, b_raw=None, eps_raw=None, log_tau=None, causal=F
         var = np.mean(lv * lv) - np.mean(lv) ** 2
         tau[h] = cov / var if var > 0 else np.nan
     return row_entropy, row_sparsity, tau
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x), the derivative of softplus, without overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x >= 0, 1.0 / (1.0 + np.exp(-np.abs(x))), np.exp(-np.abs(x)) / (1.0 + np.exp(-np.abs(x))))
+
+
+def attn_bwd_np(q, k, v, dout, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False):
+    """Gradients of L = sum(dout * out) for the forward of ``attn_fwd_np``
+    (fp64, numpy).  Returns dict(dq, dk, dv, db_raw, deps_raw, dlog_tau) with
+    the shapes of the inputs (the parameter gradients of the other branches are
+    zeros).  K/V gradients sum over the query heads that share a key/value head.
+
+    The chain rule, written out for the closed forms of the forward:
+      out_i = sum_j w_ij v_j,  w_ij = u_ij / Z_i,  Z_i = sum_j u_ij (+ 1e-9, Yat)
+      dv_j  = sum_i w_ij dout_i;   dw_ij = dout_i . v_j
+      du_ij = (dw_ij - D_i) / Z_i,  D_i = sum_j w_ij dw_ij = dout_i . out_i
+      softmax: u = e^(s - m), s = q.k / sqrt(d_k):  ds = du u
+      s^tau:   u = phi^tau, phi = softplus(s) + 1e-6:  ds = du tau u sigmoid(s) / phi,
+               dtau = sum du u ln phi, tau = softplus(log_tau) + 1
+      Yat:     u = kappa = (q.k + b)^2 / (|q - k|^2 + eps) (the clamp max(d2, 0)
+               is inactive in exact arithmetic):
+               dkappa/dq = [2 (q.k + b) k - 2 kappa (q - k)] / den,
+               dkappa/dk = [2 (q.k + b) q - 2 kappa (k - q)] / den,
+               dkappa/db = 2 (q.k + b) / den,  dkappa/deps = -kappa / den,
+               b = softplus(b_raw), eps = softplus(eps_raw), d softplus = sigmoid."""
+    variant = VARIANTS.get(variant, variant)
+    q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
+    B, Hq, Tq, dk = q.shape
+    _, Hkv, Tk, dv = v.shape
+    g = Hq // Hkv
+    kh = np.repeat(k, g, axis=1)
+    vh = np.repeat(v, g, axis=1)
+    dots = q @ np.swapaxes(kh, -1, -2)
+    allowed = np.tril(np.ones((Tq, Tk), bool)) if causal else np.ones((Tq, Tk), bool)
+    allowed = np.broadcast_to(allowed, dots.shape)
+    zeros_h = np.zeros(Hq)
+    db_raw, deps_raw, dlog_tau = zeros_h.copy(), zeros_h.copy(), zeros_h.copy()
+    if variant == YAT:
+        bias = softplus(b_raw)[None, :, None, None]
+        eps = softplus(eps_raw)[None, :, None, None]
+        d2 = (np.sum(q * q, -1, keepdims=True) + np.swapaxes(np.sum(kh * kh, -1, keepdims=True), -1, -2)
+              - 2.0 * dots)
+        den = np.maximum(d2, 0.0) + eps
+        u = np.where(allowed, (dots + bias) ** 2 / den, 0.0)
+        Z = u.sum(-1, keepdims=True) + 1e-9
+    elif variant == SOFTMAX:
+        s = np.where(allowed, dots / np.sqrt(dk), -np.inf)
+        u = np.exp(s - s.max(-1, keepdims=True))
+        Z = u.sum(-1, keepdims=True)
+    else:
+        s = dots / np.sqrt(dk)
+        tau = (softplus(log_tau) + 1.0)[None, :, None, None]
+        phi = softplus(s) + 1e-6
+        u = np.where(allowed, phi ** tau, 0.0)
+        Z = u.sum(-1, keepdims=True)
+    w = u / Z
+    out = w @ vh
+    dvh = np.swapaxes(w, -1, -2) @ dout                     # per query head
+    dw = dout @ np.swapaxes(vh, -1, -2)
+    D = np.sum(dout * out, -1, keepdims=True)
+    du = np.where(allowed, (dw - D) / Z, 0.0)
+    if variant == YAT:
+        A = np.where(allowed, 2.0 * du * (dots + bias) / den, 0.0)   # coefficient of k in dq
+        Bc = np.where(allowed, 2.0 * du * u / den, 0.0)               # coefficient of (q - k)
+        dq = (A + Bc) @ kh - Bc.sum(-1, keepdims=True) * q
+        dkh = np.swapaxes(A + Bc, -1, -2) @ q - np.swapaxes(Bc.sum(-2, keepdims=True), -1, -2) * kh
+        db_raw = sigmoid(b_raw) * np.sum(np.where(allowed, du * 2.0 * (dots + bias) / den, 0.0),
+                                         axis=(0, 2, 3))
+        deps_raw = sigmoid(eps_raw) * np.sum(du * np.where(allowed, -u / den, 0.0), axis=(0, 2, 3))
+    else:
+        if variant == SOFTMAX:
+            ds = du * u
+        else:
+            ds = np.where(allowed, du * tau * u * sigmoid(s) / phi, 0.0)
+            dlog_tau = sigmoid(log_tau) * np.sum(np.where(allowed, du * u * np.log(phi), 0.0),
+                                                 axis=(0, 2, 3))
+        ds = ds / np.sqrt(dk)
+        dq = ds @ kh
+        dkh = np.swapaxes(ds, -1, -2) @ q
+    dk_out = dkh.reshape(B, Hkv, g, Tk, dk).sum(2)
+    dv_out = dvh.reshape(B, Hkv, g, Tk, dv).sum(2)
+    return dict(dq=dq, dk=dk_out, dv=dv_out, db_raw=db_raw, deps_raw=deps_raw, dlog_tau=dlog_tau)
