@@ -204,6 +204,52 @@ int attn_telemetry(const attn_desc* desc, const void* q, const void* k, int vari
                    float* row_entropy, float* row_sparsity, float* tau_star, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* Attention backward (bf16 storage): the gradients of L = sum(dout * out)
+ * for the forward attn_fwd computed with the same desc, inputs, variant,
+ * per-head parameters and mask.
+ *
+ * The pages define the three maps (see the top of this file) and train them
+ * by automatic differentiation; the gradients here are the exact derivatives
+ * of those closed forms.  With w_ij the forward's weights, Z_i its row
+ * normaliser (Yat mass + 1e-9, s^tau mass, softmax sum_j e^(s_ij - max_i)),
+ * dp_ij = dout_i . v_j and D_i = sum_j w_ij dp_ij (= dout_i . out_i):
+ *   dv_j = sum_i w_ij dout_i, and d L / d u_ij = (dp_ij - D_i) / Z_i for the
+ *   unnormalised weight u_ij, which the chain rule carries to q, k and the
+ *   parameters through softmax's e^s, s^tau's phi(s)^tau (with
+ *   d/dtau = phi^tau ln phi) and Yat's (q.k + b)^2 / (|q - k|^2 + eps).
+ * Key/value gradients add over the query heads that share a key/value head.
+ * Masked pairs contribute nothing.  The clamp max(d2, 0) of Yat is treated
+ * as inactive (it only acts where rounding makes d2 negative, i.e. q = k,
+ * where the distance term's derivative 2 (q - k) is 0).  D is recomputed
+ * from the weights in fp32 rather than taken from the bf16 output, whose
+ * rounding would not cancel where the exact gradient does (a row whose
+ * weight sits on one key); the forward's output is therefore not an input.
+ *
+ * q, k, v        the forward's inputs, device bf16, strides of desc.
+ * dout           device bf16 [B,Hq,Tq,dv], strides desc->o_stride.
+ * mass,          the forward's row statistics, device fp32 [B,Hq,Tq],
+ * max_score      contiguous; mass always, max_score for ATTN_SOFTMAX.
+ * dq, dk, dv     device bf16 outputs laid out like q, k and v (q_stride,
+ *                k_stride, v_stride); every element is written (dk = dv = 0
+ *                when T_q == 0).  They must not alias any input.
+ * db_raw,        device fp32 [Hq] outputs for ATTN_YAT (d L / d b_raw and
+ * deps_raw       d L / d eps_raw); dlog_tau [Hq] for ATTN_STAU.  NULL means
+ * dlog_tau       "not computed"; ignored for the other maps.
+ * workspace      attn_bwd_workspace_bytes(desc, variant) bytes, 16-byte
+ *                aligned: Yat |q|^2 and |k|^2 rows, per-row D and Z, and
+ *                per-workgroup parameter sums.
+ * desc->block_rows and desc->kv_splits are forward launch options and are
+ * not used here.  Ownership, asynchrony, errors and empty problems as
+ * attn_fwd; ATTN_ERR_UNSUPPORTED for fp32 storage.  The standard maps only
+ * (not the options of attn_fwd_yat).  Summation orders are fixed: repeated
+ * calls give identical bits. */
+size_t attn_bwd_workspace_bytes(const attn_desc* desc, int variant);
+int attn_bwd(const attn_desc* desc, const void* q, const void* k, const void* v,
+             const void* dout, int variant, const float* b_raw, const float* eps_raw,
+             const float* log_tau, int causal, const float* mass, const float* max_score,
+             void* dq, void* dk, void* dv, float* db_raw, float* deps_raw, float* dlog_tau,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

@@ -261,11 +261,56 @@ def sigmoid(x):
     return np.where(x >= 0, 1.0 / (1.0 + np.exp(-np.abs(x))), np.exp(-np.abs(x)) / (1.0 + np.exp(-np.abs(x))))
 
 
-def attn_bwd_np(q, k, v, dout, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False):
+def _bwd_forward(q, k, v, dout, variant, b_raw, eps_raw, log_tau, causal):
+    """The forward quantities the backward needs (fp64): per query head the
+    repeated keys and values, q.k, the mask, the unnormalised weights u, the
+    normaliser Z, w = u / Z, dw = dout . v and D = dout . out, plus the
+    branch's own arrays (Yat: b, den; s^tau: s, tau, phi)."""
+    variant = VARIANTS.get(variant, variant)
+    q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
+    B, Hq, Tq, dk = q.shape
+    _, Hkv, Tk, dv = v.shape
+    g = Hq // Hkv
+    f = dict(variant=variant, q=q, dout=dout, g=g, shape=(B, Hq, Hkv, Tq, Tk, dk, dv))
+    f["kh"] = kh = np.repeat(k, g, axis=1)
+    vh = np.repeat(v, g, axis=1)
+    f["dots"] = dots = q @ np.swapaxes(kh, -1, -2)
+    allowed = np.tril(np.ones((Tq, Tk), bool)) if causal else np.ones((Tq, Tk), bool)
+    f["allowed"] = allowed = np.broadcast_to(allowed, dots.shape)
+    if variant == YAT:
+        f["bias"] = bias = softplus(b_raw)[None, :, None, None]
+        eps = softplus(eps_raw)[None, :, None, None]
+        d2 = (np.sum(q * q, -1, keepdims=True) + np.swapaxes(np.sum(kh * kh, -1, keepdims=True), -1, -2)
+              - 2.0 * dots)
+        f["den"] = den = np.maximum(d2, 0.0) + eps
+        u = np.where(allowed, (dots + bias) ** 2 / den, 0.0)
+        Z = u.sum(-1, keepdims=True) + 1e-9
+    elif variant == SOFTMAX:
+        s = np.where(allowed, dots / np.sqrt(dk), -np.inf)
+        u = np.exp(s - s.max(-1, keepdims=True))
+        Z = u.sum(-1, keepdims=True)
+    else:
+        f["s"] = s = dots / np.sqrt(dk)
+        f["tau"] = tau = (softplus(log_tau) + 1.0)[None, :, None, None]
+        f["phi"] = phi = softplus(s) + 1e-6
+        u = np.where(allowed, phi ** tau, 0.0)
+        Z = u.sum(-1, keepdims=True)
+    f["u"], f["Z"] = u, Z
+    f["w"] = w = u / Z
+    out = w @ vh
+    f["dw"] = dout @ np.swapaxes(vh, -1, -2)
+    f["D"] = np.sum(dout * out, -1, keepdims=True)
+    return f
+
+
+def attn_bwd_np(q, k, v, dout, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False,
+                return_abs=False):
     """Gradients of L = sum(dout * out) for the forward of ``attn_fwd_np``
     (fp64, numpy).  Returns dict(dq, dk, dv, db_raw, deps_raw, dlog_tau) with
     the shapes of the inputs (the parameter gradients of the other branches are
     zeros).  K/V gradients sum over the query heads that share a key/value head.
+    With ``return_abs`` the dict also holds the error scales of
+    ``attn_bwd_scales_np`` under the names dq_abs, dk_abs, ..., dlog_tau_abs.
 
     The chain rule, written out for the closed forms of the forward:
       out_i = sum_j w_ij v_j,  w_ij = u_ij / Z_i,  Z_i = sum_j u_ij (+ 1e-9, Yat)
@@ -280,54 +325,29 @@ def attn_bwd_np(q, k, v, dout, variant, b_raw=None, eps_raw=None, log_tau=None, 
                dkappa/dk = [2 (q.k + b) q - 2 kappa (k - q)] / den,
                dkappa/db = 2 (q.k + b) / den,  dkappa/deps = -kappa / den,
                b = softplus(b_raw), eps = softplus(eps_raw), d softplus = sigmoid."""
-    variant = VARIANTS.get(variant, variant)
-    q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
-    B, Hq, Tq, dk = q.shape
-    _, Hkv, Tk, dv = v.shape
-    g = Hq // Hkv
-    kh = np.repeat(k, g, axis=1)
-    vh = np.repeat(v, g, axis=1)
-    dots = q @ np.swapaxes(kh, -1, -2)
-    allowed = np.tril(np.ones((Tq, Tk), bool)) if causal else np.ones((Tq, Tk), bool)
-    allowed = np.broadcast_to(allowed, dots.shape)
+    f = _bwd_forward(q, k, v, dout, variant, b_raw, eps_raw, log_tau, causal)
+    variant, q, dout, kh, dots, allowed = (f[n] for n in ("variant", "q", "dout", "kh", "dots",
+                                                         "allowed"))
+    B, Hq, Hkv, Tq, Tk, dk, dv = f["shape"]
+    g = f["g"]
+    u, Z, w = f["u"], f["Z"], f["w"]
     zeros_h = np.zeros(Hq)
     db_raw, deps_raw, dlog_tau = zeros_h.copy(), zeros_h.copy(), zeros_h.copy()
-    if variant == YAT:
-        bias = softplus(b_raw)[None, :, None, None]
-        eps = softplus(eps_raw)[None, :, None, None]
-        d2 = (np.sum(q * q, -1, keepdims=True) + np.swapaxes(np.sum(kh * kh, -1, keepdims=True), -1, -2)
-              - 2.0 * dots)
-        den = np.maximum(d2, 0.0) + eps
-        u = np.where(allowed, (dots + bias) ** 2 / den, 0.0)
-        Z = u.sum(-1, keepdims=True) + 1e-9
-    elif variant == SOFTMAX:
-        s = np.where(allowed, dots / np.sqrt(dk), -np.inf)
-        u = np.exp(s - s.max(-1, keepdims=True))
-        Z = u.sum(-1, keepdims=True)
-    else:
-        s = dots / np.sqrt(dk)
-        tau = (softplus(log_tau) + 1.0)[None, :, None, None]
-        phi = softplus(s) + 1e-6
-        u = np.where(allowed, phi ** tau, 0.0)
-        Z = u.sum(-1, keepdims=True)
-    w = u / Z
-    out = w @ vh
     dvh = np.swapaxes(w, -1, -2) @ dout                     # per query head
-    dw = dout @ np.swapaxes(vh, -1, -2)
-    D = np.sum(dout * out, -1, keepdims=True)
-    du = np.where(allowed, (dw - D) / Z, 0.0)
+    du = np.where(allowed, (f["dw"] - f["D"]) / Z, 0.0)
     if variant == YAT:
+        bias, den = f["bias"], f["den"]
         A = np.where(allowed, 2.0 * du * (dots + bias) / den, 0.0)   # coefficient of k in dq
         Bc = np.where(allowed, 2.0 * du * u / den, 0.0)               # coefficient of (q - k)
         dq = (A + Bc) @ kh - Bc.sum(-1, keepdims=True) * q
         dkh = np.swapaxes(A + Bc, -1, -2) @ q - np.swapaxes(Bc.sum(-2, keepdims=True), -1, -2) * kh
-        db_raw = sigmoid(b_raw) * np.sum(np.where(allowed, du * 2.0 * (dots + bias) / den, 0.0),
-                                         axis=(0, 2, 3))
+        db_raw = sigmoid(b_raw) * np.sum(A, axis=(0, 2, 3))          # dkappa/db = A / du
         deps_raw = sigmoid(eps_raw) * np.sum(du * np.where(allowed, -u / den, 0.0), axis=(0, 2, 3))
     else:
         if variant == SOFTMAX:
             ds = du * u
         else:
+            s, tau, phi = f["s"], f["tau"], f["phi"]
             ds = np.where(allowed, du * tau * u * sigmoid(s) / phi, 0.0)
             dlog_tau = sigmoid(log_tau) * np.sum(np.where(allowed, du * u * np.log(phi), 0.0),
                                                  axis=(0, 2, 3))
@@ -336,4 +356,52 @@ def attn_bwd_np(q, k, v, dout, variant, b_raw=None, eps_raw=None, log_tau=None, 
         dkh = np.swapaxes(ds, -1, -2) @ q
     dk_out = dkh.reshape(B, Hkv, g, Tk, dk).sum(2)
     dv_out = dvh.reshape(B, Hkv, g, Tk, dv).sum(2)
-    return dict(dq=dq, dk=dk_out, dv=dv_out, db_raw=db_raw, deps_raw=deps_raw, dlog_tau=dlog_tau)
+    res = dict(dq=dq, dk=dk_out, dv=dv_out, db_raw=db_raw, deps_raw=deps_raw, dlog_tau=dlog_tau)
+    if return_abs:
+        sc = attn_bwd_scales_np(q, k, v, dout, variant, b_raw, eps_raw, log_tau, causal, _f=f)
+        res.update({n + "_abs": a for n, a in sc.items()})
+    return res
+
+
+def attn_bwd_scales_np(q, k, v, dout, variant, b_raw=None, eps_raw=None, log_tau=None,
+                       causal=False, _f=None):
+    """Error scales for tests of a finite-precision backward (not gradients):
+    the sums of ``attn_bwd_np`` with du_ij = (dw_ij - D_i) / Z_i replaced by
+    (|dw_ij| + |D_i|) / Z_i and every other factor by its absolute value.  A
+    floating-point evaluation that forms dw - D, or rounds any factor, errs by
+    a multiple of the rounding unit times this scale; it is the only scale
+    left where the two terms cancel (e.g. a row with one allowed key, whose
+    exact q and k gradients are 0)."""
+    f = _f if _f is not None else _bwd_forward(q, k, v, dout, variant, b_raw, eps_raw, log_tau,
+                                               causal)
+    variant, q, dout, kh, dots, allowed = (f[n] for n in ("variant", "q", "dout", "kh", "dots",
+                                                         "allowed"))
+    B, Hq, Hkv, Tq, Tk, dk, dv = f["shape"]
+    g = f["g"]
+    u, Z, w = f["u"], f["Z"], f["w"]
+    zeros_h = np.zeros(Hq)
+    db, de, dt = zeros_h.copy(), zeros_h.copy(), zeros_h.copy()
+    ma = np.where(allowed, (np.abs(f["dw"]) + np.abs(f["D"])) / Z, 0.0)
+    qa, ka = np.abs(q), np.abs(kh)
+    if variant == YAT:
+        bias, den = f["bias"], f["den"]
+        A = np.where(allowed, 2.0 * ma * np.abs(dots + bias) / den, 0.0)
+        Bc = np.where(allowed, 2.0 * ma * u / den, 0.0)
+        dq = (A + Bc) @ ka + Bc.sum(-1, keepdims=True) * qa
+        dkh = np.swapaxes(A + Bc, -1, -2) @ qa + np.swapaxes(Bc.sum(-2, keepdims=True), -1, -2) * ka
+        db = sigmoid(b_raw) * np.sum(A, axis=(0, 2, 3))
+        de = sigmoid(eps_raw) * np.sum(Bc, axis=(0, 2, 3)) / 2.0
+    else:
+        if variant == SOFTMAX:
+            ds = ma * u
+        else:
+            s, tau, phi = f["s"], f["tau"], f["phi"]
+            ds = np.where(allowed, ma * tau * u * sigmoid(s) / phi, 0.0)
+            dt = sigmoid(log_tau) * np.sum(np.where(allowed, ma * u * np.abs(np.log(phi)), 0.0),
+                                           axis=(0, 2, 3))
+        ds = ds / np.sqrt(dk)
+        dq = ds @ ka
+        dkh = np.swapaxes(ds, -1, -2) @ qa
+    dvh = np.swapaxes(w, -1, -2) @ np.abs(dout)
+    return dict(dq=dq, dk=dkh.reshape(B, Hkv, g, Tk, dk).sum(2),
+                dv=dvh.reshape(B, Hkv, g, Tk, dv).sum(2), db_raw=db, deps_raw=de, dlog_tau=dt)

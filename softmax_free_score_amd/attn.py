@@ -28,8 +28,8 @@ VARIANTS = {"softmax": ATTN_SOFTMAX, "yat": ATTN_YAT, "stau": ATTN_STAU}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
           -4: "ATTN_ERR_PARAM", -5: "ATTN_ERR_WORKSPACE", -6: "ATTN_ERR_HIP"}
 EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_yat",
-           "attn_telemetry_workspace_bytes", "attn_telemetry", "attn_status_string",
-           "attn_last_error")
+           "attn_telemetry_workspace_bytes", "attn_telemetry", "attn_bwd_workspace_bytes",
+           "attn_bwd", "attn_status_string", "attn_last_error")
 ATTN_YAT_MAX_POWER = 8
 
 
@@ -86,6 +86,12 @@ def load_library():
                                        vp, ctypes.c_int, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
         lib.attn_telemetry.restype = ctypes.c_int
+        lib.attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.c_int]
+        lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_bwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, ctypes.c_int, vp,
+                                 vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+        lib.attn_bwd.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -256,3 +262,53 @@ def attn_telemetry(q, k, variant, mass, max_score=None, b_raw=None, eps_raw=None
     if st != 0:
         raise AttnError(st, lib.attn_last_error().decode())
     return ent, spa, tau
+
+
+def bwd_workspace_bytes(q, k, v, variant) -> int:
+    d = make_desc(q, k, v, None)
+    return int(load_library().attn_bwd_workspace_bytes(ctypes.byref(d),
+                                                       VARIANTS.get(variant, variant)))
+
+
+def attn_bwd(q, k, v, dout, variant, mass, max_score=None, b_raw=None, eps_raw=None,
+             log_tau=None, causal=False, dq=None, dk=None, dv=None, param_grads=True,
+             workspace=None, stream=None):
+    """Enqueue the backward of a forward with the same inputs; returns a dict
+    with dq, dk, dv (bf16, laid out like q, k, v) and, when ``param_grads``,
+    the per-head parameter gradients of the variant (db_raw and deps_raw for
+    Yat, dlog_tau for s^tau; float32 [Hq]).  ``mass`` and ``max_score`` are
+    the forward's row statistics; ``dout`` is dL/dout [B, Hq, Tq, dv]."""
+    lib = load_library()
+    variant = VARIANTS.get(variant, variant)
+    B, Hq, Tq, _ = q.shape
+    if dout.dim() != 4 or tuple(dout.shape) != (B, Hq, Tq, v.shape[3]):
+        raise ValueError("dout must be [B, Hq, Tq, dv]")
+    grads = {}
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_strided(like.shape, like.stride(), dtype=like.dtype,
+                                    device=like.device)
+        elif t.shape != like.shape or t.stride() != like.stride() or t.dtype != like.dtype:
+            raise ValueError(f"{name} must have the shape, strides and dtype of its input")
+        grads[name] = t
+    f32 = dict(dtype=torch.float32, device=q.device)
+    want_p = bool(param_grads)
+    grads["db_raw"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_YAT else None
+    grads["deps_raw"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_YAT else None
+    grads["dlog_tau"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_STAU else None
+    desc = make_desc(q, k, v, dout)
+    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc), variant))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    st = lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                      variant, _ptr(b_raw), _ptr(eps_raw), _ptr(log_tau), int(bool(causal)),
+                      _ptr(mass), _ptr(max_score), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                      _ptr(grads["dv"]), _ptr(grads["db_raw"]), _ptr(grads["deps_raw"]),
+                      _ptr(grads["dlog_tau"]), _ptr(workspace), ws_bytes,
+                      ctypes.c_void_p(stream) if stream else None)
+    if st != 0:
+        raise AttnError(st, lib.attn_last_error().decode())
+    return grads

@@ -37,8 +37,10 @@ def _units():
     units = [("attn_api", "attn_api.cpp", [])]
     units.append(("attn_f32", "attn_f32.hip", []))
     units.append(("attn_combine", "attn_combine.hip", []))
+    units.append(("attn_bwd_aux", "attn_bwd_aux.hip", []))
     for dk in (16, 32, 64, 128):
         units.append((f"attn_bf16_dk{dk}", "attn_bf16.hip", [f"-DSFS_DK={dk}"]))
+        units.append((f"attn_bwd_dk{dk}", "attn_bwd.hip", [f"-DSFS_DK={dk}"]))
     return units
 
 

@@ -336,6 +336,140 @@ int attn_telemetry(const attn_desc* d, const void* q, const void* k, int variant
   return ATTN_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the backward: Yat |k|^2 and |q|^2 rows, the row values D and
+// Z, and the parameter sums; each region 256-byte aligned.
+struct BwdWs {
+  size_t nk, nq, rd, rz, prm, total;
+};
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+BwdWs bwd_ws(const attn_desc* d, int variant) {
+  BwdWs w{};
+  const size_t rows_q = (size_t)(d->B * d->Hq * sfs::nk_pitch(d->Tq)) * 4;
+  const size_t n_qt = (size_t)((d->Tq + sfs::kBwdQRows - 1) / sfs::kBwdQRows);
+  size_t off = 0;
+  w.nk = off;
+  if (variant == ATTN_YAT) off += align256((size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4);
+  w.nq = off;
+  if (variant == ATTN_YAT) off += align256(rows_q);
+  w.rd = off;
+  off += align256(rows_q);
+  w.rz = off;
+  off += align256(rows_q);
+  w.prm = off;
+  if (variant != ATTN_SOFTMAX) off += (size_t)(d->Hq * d->B) * n_qt * 2 * sizeof(double);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(const attn_desc* d, int variant) {
+  if (!d || d->dtype != ATTN_BF16) return 0;
+  if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0) return 0;
+  if (variant < ATTN_SOFTMAX || variant > ATTN_STAU) return 0;
+  return bwd_ws(d, variant).total;
+}
+
+int attn_bwd(const attn_desc* d, const void* q, const void* k, const void* v,
+             const void* dout, int variant, const float* b_raw, const float* eps_raw,
+             const float* log_tau, int causal, const float* mass, const float* max_score,
+             void* dq, void* dk, void* dv, float* db_raw, float* deps_raw, float* dlog_tau,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (d && d->dtype != ATTN_BF16) {
+    set_error("the backward is built for bf16 storage");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  bool empty = false;
+  const int64_t need = d ? (int64_t)attn_bwd_workspace_bytes(d, variant) : 0;
+  // dout takes the place of out (o_stride describes it)
+  int st = validate(d, q, k, v, variant, b_raw, eps_raw, log_tau, causal, dout, mass, max_score,
+                    workspace, workspace_bytes, false, &empty, need);
+  if (st != ATTN_OK) return st;
+  if (!empty) {
+    if (!dq || !dk || !dv || !mass || (variant == ATTN_SOFTMAX && !max_score)) {
+      set_error("the backward needs dq, dk, dv, the forward's mass and, for softmax, "
+                "its max_score");
+      return ATTN_ERR_NULL;
+    }
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) {
+      set_error("dq, dk and dv must be 16-byte aligned");
+      return ATTN_ERR_UNSUPPORTED;
+    }
+    for (const float* t : {db_raw, deps_raw, dlog_tau})
+      if (reinterpret_cast<uintptr_t>(t) & 3u) {
+        set_error("parameter gradients must be 4-byte aligned");
+        return ATTN_ERR_UNSUPPORTED;
+      }
+  }
+  if (empty && d->B > 0) {
+    // T_q == 0: no query rows, so dk and dv are zero; they are still written
+    if (!k || !v || !dk || !dv) {
+      set_error("k, v, dk and dv are required");
+      return ATTN_ERR_NULL;
+    }
+    if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv) ||
+        !strides_ok(d->k_stride, d->Tk, d->dk, 2) || !strides_ok(d->v_stride, d->Tk, d->dv, 2)) {
+      set_error("k, v, dk, dv must be 16-byte aligned with valid strides");
+      return ATTN_ERR_UNSUPPORTED;
+    }
+  } else if (empty) {
+    return ATTN_OK;
+  }
+
+  sfs::BwdProblem p{};
+  p.q = q; p.k = k; p.v = v; p.dout = dout;
+  p.dq = dq; p.dk_ = dk; p.dv_ = dv;
+  p.b_raw = b_raw; p.eps_raw = eps_raw; p.log_tau = log_tau;
+  p.mass = mass; p.max_score = max_score;
+  p.db_raw = db_raw; p.deps_raw = deps_raw; p.dlog_tau = dlog_tau;
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = d->q_stride[i]; p.ks[i] = d->k_stride[i];
+    p.vs[i] = d->v_stride[i]; p.os[i] = d->o_stride[i];
+  }
+  p.B = (int)d->B; p.Hq = (int)d->Hq; p.Hkv = (int)d->Hkv;
+  p.Tq = (int)d->Tq; p.Tk = (int)d->Tk; p.dk = (int)d->dk; p.dv = (int)d->dv;
+  p.variant = variant;
+  p.causal = causal ? 1 : 0;
+  const BwdWs w = bwd_ws(d, variant);
+  char* ws = static_cast<char*>(workspace);
+  p.nk = reinterpret_cast<float*>(ws + w.nk);
+  p.nq = reinterpret_cast<float*>(ws + w.nq);
+  p.row_d = reinterpret_cast<float*>(ws + w.rd);
+  p.row_z = reinterpret_cast<float*>(ws + w.rz);
+  const bool params = (variant == ATTN_YAT && (db_raw || deps_raw)) ||
+                      (variant == ATTN_STAU && dlog_tau);
+  p.prm_part = params ? reinterpret_cast<double*>(ws + w.prm) : nullptr;
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.Tq > 0) e = sfs::launch_bwd_rows(p, s);  // (no rows: an empty grid)
+    if (e == hipSuccess) {
+      switch (p.dk) {
+        case 16: e = sfs::launch_bwd_bf16_dk16(p, s); break;
+        case 32: e = sfs::launch_bwd_bf16_dk32(p, s); break;
+        case 64: e = sfs::launch_bwd_bf16_dk64(p, s); break;
+        default: e = sfs::launch_bwd_bf16_dk128(p, s); break;
+      }
+    }
+    if (e == hipSuccess && params) e = sfs::launch_bwd_params(p, s);
+  }
+  if (e != hipSuccess) {
+    char msg[256];
+    std::snprintf(msg, sizeof msg, "HIP: %s (%s)", hipGetErrorName(e), hipGetErrorString(e));
+    set_error(msg);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -47,7 +47,7 @@
 //     (softmax maximum) or once at the end (mass, max_score).
 //   * Ragged tails: buffer loads past the end of a (b, h) slice return 0; the
 //     mask zeroes keys >= T_k; query rows >= T_q are computed but not stored.
-#include "attn_launch.h"
+#include "bf16_common.h"
 
 #include <type_traits>
 
@@ -60,94 +60,6 @@
 
 namespace sfs {
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-// Buffer-resource word 3 for raw (unformatted) dword access on gfx9.
-constexpr int kRsrcWord3 = 0x00020000;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
-}
-__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  bf16x2 v;
-  v[0] = (__bf16)lo;  // round to nearest even
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(unsigned, v);
-}
-// log(1 + e^x) without overflow (fp32 library calls; used once per head).
-__device__ __forceinline__ float softplus_precise(float x) {
-  return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-}
-// Byte size of a (b, h) slice with rows of `d` elements at `row_stride`.
-__device__ __forceinline__ uint32_t slice_bytes(int rows, int64_t row_stride, int d) {
-  return (uint32_t)(((int64_t)(rows - 1) * row_stride + d) * 2);
-}
-// Row position inside a 32-row block of the K tile in LDS: bits 2 and 3 swapped.
-__device__ __forceinline__ int k_lds_row(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-// Diagonal of the 32x32 accumulator of X X^T: column n = col sits in the lane
-// half (col >> 2) & 1, element 4 (col >> 3) + (col & 3).
-__device__ __forceinline__ bool holds_diag(int col, int half) { return ((col >> 2) & 1) == half; }
-__device__ __forceinline__ float diag_of(const f32x16& g, int col) {
-  const int r = 4 * (col >> 3) + (col & 3);
-  float d = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) d = (i == r) ? g[i] : d;
-  return d;
-}
-
-// |k_j|^2 for every key row, by the same MFMA sequence as the score tile.
-// One wave per 32 rows; grid (ceil(T/128), H, B), 256 threads.
-template <int DK>
-__global__ __launch_bounds__(256) void row_norms_bf16(const unsigned short* x, int64_t s0,
-                                                      int64_t s1, int64_t s2, int H, int T,
-                                                      float* out) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 31, half = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int row = blockIdx.x * 128 + 32 * w + col;
-  const unsigned short* base = x + (int64_t)b * s0 + (int64_t)h * s1;
-  const uint32_t bytes = slice_bytes(T, s2, DK);
-  const rsrc_t r = make_rsrc(base, bytes);
-  const uint32_t off = row < T ? (uint32_t)(((int64_t)row * s2 + 8 * half) * 2) : bytes;
-  f32x16 g = {};
-#pragma unroll
-  for (int s = 0; s < DK / 16; ++s)
-    g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
-               __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
-  if (row < T && holds_diag(col, half))
-    out[((int64_t)b * H + h) * nk_pitch(T) + row] = diag_of(g, col);
-}
-
-// Partner-lane exchange for row statistics: lanes l and l ^ 32 hold the same
-// query.  v_permlane32_swap hands every lane both halves' values.
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return __builtin_bit_cast(float, (unsigned)s[0]) + __builtin_bit_cast(float, (unsigned)s[1]);
-}
-__device__ __forceinline__ float pair_max(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)s[0]), __builtin_bit_cast(float, (unsigned)s[1]));
-}
 
 // Softmax keeps exponentials relative to a reference maximum that is only
 // moved when a tile's maximum exceeds it by more than this (log2 units):

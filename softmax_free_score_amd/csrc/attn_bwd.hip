@@ -1,0 +1,763 @@
+// attn_bwd.hip -- attention backward for bf16 storage on gfx950.
+//
+// Compiled once per key width: -DSFS_DK=16|32|64|128.
+//
+// For L = sum(dout * out) and the forward defined in attn_bf16.hip, with the
+// row values D_i = sum_j w_ij dp_ij (= dout_i . out_i; computed here from the
+// recomputed weights) and the normaliser Z_i of the forward (see
+// attn_bwd_aux.hip), every allowed pair (i, j) has
+//   w_ij  the forward's weight,  dp_ij = dout_i . v_j,
+//   du_ij = (dp_ij - D_i) / Z_i  (d L / d of the unnormalised weight u_ij),
+// and the gradients are
+//   dv_j = sum_i w_ij dout_i,
+//   dq_i = sum_j g_ij k_j - c_i q_i,   dk_j = sum_i g_ij q_i - c'_j k_j,
+// with the "gradient score" g and the corrections c per map:
+//   softmax  u = e^(s - max), s = q.k / sqrt(d_k):
+//            g = w (dp - D) / sqrt(d_k), c = 0;
+//   s^tau    u = phi^tau, phi = softplus(s) + 1e-6:
+//            g = w (dp - D) tau sigmoid(s) / phi / sqrt(d_k), c = 0;
+//   Yat      u = kappa = (q.k + b)^2 / den, den = |q|^2 + |k|^2 - 2 q.k + eps
+//            (d den / d q = 2 (q - k)):
+//            g = A + B, A = 2 du (q.k + b) / den, B = 2 du kappa / den,
+//            c_i = sum_j B_ij, c'_j = sum_i B_ij,
+// i.e. d kappa / d q = [2 (q.k + b) k - 2 kappa (q - k)] / den.
+// ("Softmax-Free Attention in JAX/Flax NNX", "One module, two compatibility
+// functions", for the Yat map; "NNX Scaled Dot-Product Attention", displayed
+// equation, for softmax; the "s^tau" forum post, core formula, for s^tau.)
+//
+// Design (gfx950 / CDNA4, wave64, v_mfma_f32_32x32x16_bf16 throughout):
+//   * Two kernels, no atomics: attn_bwd_kv owns 128 keys of one (b, kv head)
+//     per workgroup (32 per wave, their k and v rows in registers) and streams
+//     32-query tiles of every query head of the group; attn_bwd_q owns 128
+//     query rows of one (b, h) (32 per wave) and streams 32-key tiles.  Each
+//     recomputes the score tile (and dp) it needs, so both the score and the
+//     dp products are taken twice; in exchange every output is written once,
+//     in a fixed summation order.
+//   * attn_bwd_kv computes S = Q K^T with the query rows of the tile in LDS
+//     (rows permuted by swapping bits 2 and 3, as the forward does for keys),
+//     so the accumulator of lane (half, col) holds key col and queries
+//     16 (r / 8) + 8 half + r % 8 in natural order: packed to bf16 it is the B
+//     operand of dV^T += dO^T P and dK^T += Q^T G, whose A operands (dO^T,
+//     Q^T, queries contiguous) are written transposed into LDS on the way in.
+//   * attn_bwd_q is the mirror image: S^T = K Q^T and dP^T = V dO^T with the
+//     lane's query fragments in registers, then dQ^T += K^T G^T with K^T in
+//     LDS.
+//   * Yat's subtraction of c q (or c' k) cancels against the B part of the
+//     product g k exactly where q = k only if both use the same B values.
+//     g is rounded to bf16 for the matrix core; the correction uses
+//     B' = bf16(g) - A, so that the kernel computes A k + B' (k - q) with the
+//     difference (k - q) formed in exact arithmetic.
+//   * Yat |q|^2 and |k|^2 come from the same MFMA pre-pass as the forward's,
+//     so d2 = |q|^2 + |k|^2 - 2 q.k cancels to exactly 0 for a key equal to
+//     its query.
+//   * Parameter gradients: attn_bwd_q sums A and B (Yat) or
+//     w (dp - D) log2(phi) (s^tau) per workgroup; a last kernel adds the
+//     workgroup sums per head in a fixed order.
+#include "bf16_common.h"
+
+#include <type_traits>
+
+#ifndef SFS_DK
+#error "compile with -DSFS_DK=16, 32, 64 or 128"
+#endif
+
+#define SFS_CAT2(a, b) a##b
+#define SFS_CAT(a, b) SFS_CAT2(a, b)
+
+namespace sfs {
+namespace {
+
+__device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Per-head constants of a map.
+struct HeadC {
+  float bias, eps, tau, scale, c_sm;
+};
+template <int VAR, int DK>
+__device__ __forceinline__ HeadC head_consts(const BwdProblem& p, int h) {
+  HeadC c{0.f, 0.f, 0.f, 1.0f / sqrtf((float)DK), 0.f};
+  c.c_sm = c.scale * kLog2e;
+  if (is_yat(VAR)) {
+    c.bias = softplus_precise(p.b_raw[h]);
+    c.eps = softplus_precise(p.eps_raw[h]);
+  } else if (VAR == kStau) {
+    c.tau = softplus_precise(p.log_tau[h]) + 1.f;
+  }
+  return c;
+}
+
+// One pair: from sd = q.k, dp = dout.v, the row's D and normaliser Z (softmax:
+// L, the log2 normaliser) and, for Yat, nqk = |q|^2 + |k|^2, the weight w, the
+// gradient score g (before the 1/sqrt(d_k) of softmax and s^tau) and the
+// terms of the Yat correction and parameter sums (a, bc) or the s^tau one (lt).
+template <int VAR>
+__device__ __forceinline__ void pair_terms(float sd, float dp, float D, float Z, float nqk,
+                                           const HeadC& hc, float& w, float& g, float& a,
+                                           float& bc, float& lt) {
+  if constexpr (is_yat(VAR)) {
+    const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
+    const float u = sd + hc.bias;
+    const float kap = u * u * rden;
+    w = kap * Z;
+    const float t = 2.f * (dp - D) * Z * rden;
+    a = t * u;
+    bc = t * kap;
+    g = a + bc;
+    lt = 0.f;
+  } else if constexpr (VAR == kSoftmax) {
+    w = __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
+    g = w * (dp - D);
+    a = bc = lt = 0.f;
+  } else {
+    const float s = sd * hc.scale;
+    // softplus as the forward takes it: max(s, 0) + log1p(e), e = exp(-|s|),
+    // with the rounding error of 1 + e corrected to first order
+    const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+    const float u1 = 1.f + e;
+    const float c = (u1 - 1.f) - e;
+    const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
+    const float phi = sp + 1e-6f;
+    const float lp = __builtin_amdgcn_logf(phi);  // log2(phi)
+    w = __builtin_amdgcn_exp2f(hc.tau * lp) * Z;
+    const float sig = (s >= 0.f ? 1.f : e) * __builtin_amdgcn_rcpf(u1);  // sigmoid(s)
+    const float dw = w * (dp - D);
+    g = dw * hc.tau * sig * __builtin_amdgcn_rcpf(phi);
+    lt = dw * lp;
+    a = bc = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 4 waves x 32 keys; 32-query tiles of every query head of the group.
+template <int VAR, int DK, int DV>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv(BwdProblem p) {
+  constexpr int NW = 4, NT = 64 * NW, BK = 32 * NW, BQ = 32;
+  constexpr int KS = DK / 16, VS = DV / 16;
+  constexpr int DKP = DK < 32 ? 32 : DK, DVP = DV < 32 ? 32 : DV;
+  constexpr int KB = DKP / 32, VB = DVP / 32;
+  constexpr int QLD = DK + 8, OLD = DV + 8, TLD = BQ + 8;
+  constexpr int Q_UNITS = (BQ / 4) * (DK / 8), O_UNITS = (BQ / 4) * (DV / 8);
+  constexpr int UNITS = Q_UNITS + O_UNITS;
+  constexpr int PER_T = (UNITS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) unsigned short sQ[2][BQ * QLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sQt[2][DKP * TLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sO[2][BQ * OLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sOt[2][DVP * TLD];
+  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sZ[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sNQ[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  // Workgroup -> (key tile, batch, kv head), heads fastest.  With a causal
+  // mask the first key tiles have the most queries and go first.
+  const int nbh = p.B * p.Hkv;
+  const int kt = blockIdx.x / nbh;
+  const int bh = blockIdx.x - kt * nbh;
+  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int g = p.Hq / p.Hkv;
+  const int k0 = kt * BK, kw = k0 + 32 * w, my_k = kw + col;
+
+  const unsigned short* kbase =
+      (const unsigned short*)p.k + (int64_t)b * p.ks[0] + (int64_t)hk * p.ks[1];
+  const unsigned short* vbase =
+      (const unsigned short*)p.v + (int64_t)b * p.vs[0] + (int64_t)hk * p.vs[1];
+  const uint32_t k_bytes = slice_bytes(p.Tk, p.ks[2], DK);
+  const uint32_t v_bytes = slice_bytes(p.Tk, p.vs[2], DV);
+  const uint32_t q_bytes = slice_bytes(p.Tq, p.qs[2], DK);
+  const uint32_t o_bytes = slice_bytes(p.Tq, p.os[2], DV);
+  const int qst = (int)p.qs[2], ost = (int)p.os[2];
+
+  // This lane's key and value rows: the B operands of S = Q K^T and dP = dO V^T.
+  bf16x8 kf[KS], vf[VS];
+  {
+    const rsrc_t rk = make_rsrc(kbase, k_bytes);
+    const rsrc_t rv = make_rsrc(vbase, v_bytes);
+    const uint32_t ko = my_k < p.Tk ? (uint32_t)(((int64_t)my_k * p.ks[2] + 8 * half) * 2)
+                                    : k_bytes;
+    const uint32_t vo = my_k < p.Tk ? (uint32_t)(((int64_t)my_k * p.vs[2] + 8 * half) * 2)
+                                    : v_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = __builtin_bit_cast(bf16x8, ld128(rk, ko + 32 * s));
+#pragma unroll
+    for (int s = 0; s < VS; ++s) vf[s] = __builtin_bit_cast(bf16x8, ld128(rv, vo + 32 * s));
+  }
+  const int n_qt = (p.Tq + BQ - 1) / BQ;
+  const int qt0 = p.causal ? k0 / BQ : 0;  // causal: T_q == T_k, so qt0 < n_qt
+  const int per_head = n_qt - qt0;
+  const int n_it = g * per_head;           // 0 when T_q == 0: only zeros are stored
+  const int64_t qpitch = nk_pitch(p.Tq);
+  float nk = 0.f;
+  if (is_yat(VAR) && n_it > 0 && my_k < p.Tk)
+    nk = p.nk[((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) + my_k];
+
+  // Staging registers for the next query tile.
+  u32x4 st[PER_T][4];
+  float st_d = 0.f, st_z = 0.f, st_nq = 0.f;
+  auto load = [&](int it) {
+    const int gi = it / per_head, qt = qt0 + it - gi * per_head;
+    const int h = hk * g + gi, qb = qt * BQ;
+    const rsrc_t rq = make_rsrc((const unsigned short*)p.q + (int64_t)b * p.qs[0] +
+                                    (int64_t)h * p.qs[1], q_bytes);
+    const rsrc_t ro = make_rsrc((const unsigned short*)p.dout + (int64_t)b * p.os[0] +
+                                    (int64_t)h * p.os[1], o_bytes);
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < Q_UNITS) {
+        const int g4 = u % (BQ / 4), c = u / (BQ / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = qb + 4 * g4 + r;
+          st[i][r] = ld128(rq, row < p.Tq ? (uint32_t)((row * qst + 8 * c) * 2) : q_bytes);
+        }
+      } else if (u < UNITS) {
+        const int u2 = u - Q_UNITS;
+        const int g4 = u2 % (BQ / 4), c = u2 / (BQ / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = qb + 4 * g4 + r;
+          st[i][r] = ld128(ro, row < p.Tq ? (uint32_t)((row * ost + 8 * c) * 2) : o_bytes);
+        }
+      }
+    }
+    if (tid < BQ) {
+      const int64_t idx = ((int64_t)b * p.Hq + h) * qpitch + qb + tid;
+      st_d = p.row_d[idx];
+      st_z = p.row_z[idx];
+      if (is_yat(VAR)) st_nq = p.nq[idx];
+    }
+  };
+  // 4 rows x 8 columns -> 4 rows of the row-major tile (rows permuted) and
+  // 8 rows of 4 of the transposed one.
+  auto put = [&](const u32x4* rows, int g4, int c, unsigned short* R, int ld,
+                 unsigned short* Tr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *(u32x4*)&R[k_lds_row(4 * g4 + r) * ld + 8 * c] = rows[r];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned a0 = rows[0][e], a1 = rows[1][e], a2 = rows[2][e], a3 = rows[3][e];
+      u32x2 lo, hi;
+      lo[0] = (a0 & 0xffffu) | (a1 << 16);
+      lo[1] = (a2 & 0xffffu) | (a3 << 16);
+      hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+      hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+      *(u32x2*)&Tr[(8 * c + 2 * e) * TLD + 4 * g4] = lo;
+      *(u32x2*)&Tr[(8 * c + 2 * e + 1) * TLD + 4 * g4] = hi;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < Q_UNITS) {
+        put(st[i], u % (BQ / 4), u / (BQ / 4), sQ[buf], QLD, sQt[buf]);
+      } else if (u < UNITS) {
+        const int u2 = u - Q_UNITS;
+        put(st[i], u2 % (BQ / 4), u2 / (BQ / 4), sO[buf], OLD, sOt[buf]);
+      }
+    }
+    if (tid < BQ) {
+      sD[buf][tid] = st_d;
+      sZ[buf][tid] = st_z;
+      sNQ[buf][tid] = st_nq;
+    }
+  };
+
+  f32x16 accK[KB], accV[VB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) accK[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < VB; ++i) accV[i] = f32x16{};
+  float corr = 0.f;  // Yat: sum over the lane's queries of B' = bf16(g) - A
+  HeadC hc{};
+
+  // Scores of one tile -> packed weights (pw) and gradient scores (pg).
+  auto scores = [&](auto mask_tag, int buf, int qb, u32x4* pw, u32x4* pg) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 sacc = {}, pacc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQ[buf][col * QLD + 16 * s + 8 * half]),
+                    kf[s], sacc);
+#pragma unroll
+    for (int s = 0; s < VS; ++s)
+      pacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sO[buf][col * OLD + 16 * s + 8 * half]),
+                    vf[s], pacc);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // accumulator elements 8 s .. 8 s + 7: queries qb + 16 s + 8 half + 0..7
+      const int q8 = 16 * s + 8 * half;
+      const f32x4 d0 = *(const f32x4*)&sD[buf][q8], d1 = *(const f32x4*)&sD[buf][q8 + 4];
+      const f32x4 z0 = *(const f32x4*)&sZ[buf][q8], z1 = *(const f32x4*)&sZ[buf][q8 + 4];
+      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
+      if (is_yat(VAR)) {
+        n0 = *(const f32x4*)&sNQ[buf][q8];
+        n1 = *(const f32x4*)&sNQ[buf][q8 + 4];
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float wv[2], gv[2], av[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int e = 2 * e2 + o, r = 8 * s + e;
+          const float D = e < 4 ? d0[e] : d1[e - 4];
+          const float Z = e < 4 ? z0[e] : z1[e - 4];
+          const float nq = e < 4 ? n0[e] : n1[e - 4];
+          float bc, lt;
+          pair_terms<VAR>(sacc[r], pacc[r], D, Z, nq + nk, hc, wv[o], gv[o], av[o], bc, lt);
+          if (MASK) {
+            const int qi = qb + q8 + e;
+            const bool ok = qi < p.Tq && !(p.causal && my_k > qi);
+            wv[o] = ok ? wv[o] : 0.f;
+            gv[o] = ok ? gv[o] : 0.f;
+            av[o] = ok ? av[o] : 0.f;
+          }
+        }
+        pw[s][e2] = pack_bf16(wv[0], wv[1]);
+        pg[s][e2] = pack_bf16(gv[0], gv[1]);
+        if (is_yat(VAR)) corr += (bf16_lo(pg[s][e2]) - av[0]) + (bf16_hi(pg[s][e2]) - av[1]);
+      }
+    }
+  };
+  // dV^T += dO^T P, dK^T += Q^T G (keys are the columns)
+  auto accumulate = [&](int buf, const u32x4* pw, const u32x4* pg) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, pw[s]);
+      const bf16x8 bg = __builtin_bit_cast(bf16x8, pg[s]);
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        accV[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sOt[buf][(32 * i + col) * TLD + 16 * s + 8 * half]),
+                         bw, accV[i]);
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        accK[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQt[buf][(32 * i + col) * TLD + 16 * s + 8 * half]),
+                         bg, accK[i]);
+    }
+  };
+
+  // Stage it is written at the start of iteration it - 1 (the prologue for
+  // it = 0, 1) from registers loaded during iteration it - 2, after that
+  // iteration's scores, so that the staging registers and the score tiles
+  // are not live at the same time.
+  if (n_it > 0) {
+    load(0);
+    store(0);
+    if (n_it > 1) load(1);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    // stage buf ^ 1 was last read in iteration it - 1, finished by all waves
+    if (it + 1 < n_it) store(buf ^ 1);
+    const int gi = it / per_head, qt = qt0 + it - gi * per_head;
+    const int qb = qt * BQ;
+    if (it == 0 || qt == qt0) hc = head_consts<VAR, DK>(p, hk * g + gi);
+    // a tile whose every query precedes every key of this wave: nothing to do
+    const bool active = !(p.causal && qb + BQ - 1 < kw);
+    u32x4 pw[2], pg[2];
+    if (active) {
+      const bool need_mask = (p.causal && qb < kw + 32) || qb + BQ > p.Tq;
+      if (need_mask) scores(std::true_type{}, buf, qb, pw, pg);
+      else scores(std::false_type{}, buf, qb, pw, pg);
+    }
+    if (it + 2 < n_it) load(it + 2);
+    if (active) accumulate(buf, pw, pg);
+    __syncthreads();
+  }
+
+  if (is_yat(VAR)) corr = pair_sum(corr);
+  if (my_k < p.Tk) {
+    unsigned short* dkrow = (unsigned short*)p.dk_ + (int64_t)b * p.ks[0] +
+                            (int64_t)hk * p.ks[1] + (int64_t)my_k * p.ks[2];
+    unsigned short* dvrow = (unsigned short*)p.dv_ + (int64_t)b * p.vs[0] +
+                            (int64_t)hk * p.vs[1] + (int64_t)my_k * p.vs[2];
+    const unsigned short* krow = kbase + (int64_t)my_k * p.ks[2];
+    const float sc = is_yat(VAR) ? 1.f : 1.0f / sqrtf((float)DK);
+    // accumulator element 4 g4 + e of block i: row 32 i + 8 g4 + 4 half + e
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * i + 8 * g4 + 4 * half;
+        if (d0 < DK) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = accK[i][4 * g4 + e] * sc;
+          if (is_yat(VAR)) {
+            const u32x2 kk = *(const u32x2*)&krow[d0];
+            x[0] -= corr * bf16_lo(kk[0]);
+            x[1] -= corr * bf16_hi(kk[0]);
+            x[2] -= corr * bf16_lo(kk[1]);
+            x[3] -= corr * bf16_hi(kk[1]);
+          }
+          u32x2 o;
+          o[0] = pack_bf16(x[0], x[1]);
+          o[1] = pack_bf16(x[2], x[3]);
+          *(u32x2*)&dkrow[d0] = o;
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < VB; ++i)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * i + 8 * g4 + 4 * half;
+        if (d0 < DV) {
+          u32x2 o;
+          o[0] = pack_bf16(accV[i][4 * g4], accV[i][4 * g4 + 1]);
+          o[1] = pack_bf16(accV[i][4 * g4 + 2], accV[i][4 * g4 + 3]);
+          *(u32x2*)&dvrow[d0] = o;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ and the parameter sums: 4 waves x 32 query rows; 32-key tiles.
+//
+// DELTA = true is a pass of its own before the gradient kernels: the same
+// score tiles give D_i = sum_j w_ij dp_ij in fp32 from the weights as this
+// file computes them.  In exact arithmetic D_i = dout_i . out_i, but the
+// stored bf16 output is off by about 2^-9 |dp|, and every gradient score of
+// the row carries that error through (dp - D): where the exact gradient
+// cancels (a row whose weight sits on one key: dp - D = dp (1 - w), w ~ 1)
+// it would be left at 2^-9 of the terms, and for Yat it is multiplied by
+// d ln(kappa) / d q = 2 k / (q.k + b) - 2 (q - k) / den, unbounded where
+// q.k + b -> 0.  With D from the same fp32 weights the cancellation is exact
+// up to fp32 rounding.
+template <int VAR, int DK, int DV, bool DELTA>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(2, 2))) void attn_bwd_q(BwdProblem p) {
+  constexpr int NW = 4, NT = 64 * NW, BM = 32 * NW, BN = 32;
+  static_assert(BM == kBwdQRows, "query rows per workgroup");
+  constexpr int KS = DK / 16, VS = DV / 16;
+  constexpr int DKP = DK < 32 ? 32 : DK;
+  constexpr int KB = DKP / 32;
+  constexpr int KLD = DK + 8, VLD = DV + 8, TLD = BN + 8;
+  constexpr int K_UNITS = (BN / 4) * (DK / 8), V_UNITS = (BN / 4) * (DV / 8);
+  constexpr int UNITS = K_UNITS + V_UNITS;
+  constexpr int PER_T = (UNITS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) unsigned short sK[2][BN * KLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sKt[2][DELTA ? 8 : DKP * TLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[2][BN * VLD];
+  __shared__ __attribute__((aligned(16))) float sNK[2][BN];
+  __shared__ float sPrm[NW][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int n_qt = (p.Tq + BM - 1) / BM;
+  const int nbh = p.B * p.Hq;
+  int qt = blockIdx.x / nbh;
+  const int bh = blockIdx.x - qt * nbh;
+  if (p.causal) qt = n_qt - 1 - qt;  // longest rows first
+  const int b = bh / p.Hq, h = bh - b * p.Hq;
+  const int hk = h / (p.Hq / p.Hkv);
+  const int q0 = qt * BM, qw = q0 + 32 * w, my_q = qw + col;
+
+  const unsigned short* qbase =
+      (const unsigned short*)p.q + (int64_t)b * p.qs[0] + (int64_t)h * p.qs[1];
+  const unsigned short* obase =
+      (const unsigned short*)p.dout + (int64_t)b * p.os[0] + (int64_t)h * p.os[1];
+  const uint32_t q_bytes = slice_bytes(p.Tq, p.qs[2], DK);
+  const uint32_t o_bytes = slice_bytes(p.Tq, p.os[2], DV);
+  const uint32_t k_bytes = slice_bytes(p.Tk, p.ks[2], DK);
+  const uint32_t v_bytes = slice_bytes(p.Tk, p.vs[2], DV);
+  const rsrc_t rk = make_rsrc((const unsigned short*)p.k + (int64_t)b * p.ks[0] +
+                                  (int64_t)hk * p.ks[1], k_bytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)p.v + (int64_t)b * p.vs[0] +
+                                  (int64_t)hk * p.vs[1], v_bytes);
+  const int kst = (int)p.ks[2], vst = (int)p.vs[2];
+
+  // This lane's query and output-gradient rows: B operands of S^T and dP^T.
+  bf16x8 qf[KS], of[VS];
+  {
+    const rsrc_t rq = make_rsrc(qbase, q_bytes);
+    const rsrc_t ro = make_rsrc(obase, o_bytes);
+    const uint32_t qo = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
+                                    : q_bytes;
+    const uint32_t oo = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.os[2] + 8 * half) * 2)
+                                    : o_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, qo + 32 * s));
+#pragma unroll
+    for (int s = 0; s < VS; ++s) of[s] = __builtin_bit_cast(bf16x8, ld128(ro, oo + 32 * s));
+  }
+  float D = 0.f, Z = 0.f, nq = 0.f;
+  const int64_t row_idx = ((int64_t)b * p.Hq + h) * nk_pitch(p.Tq) + my_q;
+  if (my_q < p.Tq) {
+    const int64_t idx = row_idx;
+    if (!DELTA) D = p.row_d[idx];
+    Z = p.row_z[idx];
+    if (is_yat(VAR)) nq = p.nq[idx];
+  }
+  const HeadC hc = head_consts<VAR, DK>(p, h);
+  const float* nk_slice =
+      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+
+  const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  u32x4 st[PER_T][4];
+  f32x4 st_nk = {0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < K_UNITS) {
+        const int g4 = u % (BN / 4), c = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = k0 + 4 * g4 + r;
+          st[i][r] = ld128(rk, row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes);
+        }
+      } else if (u < UNITS) {
+        const int u2 = u - K_UNITS;
+        const int g4 = u2 % (BN / 4), c = u2 / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = k0 + 4 * g4 + r;
+          st[i][r] = ld128(rv, row < p.Tk ? (uint32_t)((row * vst + 8 * c) * 2) : v_bytes);
+        }
+      }
+    }
+    // the |k|^2 slice is padded to a multiple of 64 rows
+    if (is_yat(VAR) && tid < BN / 4) st_nk = *(const f32x4*)(nk_slice + k0 + 4 * tid);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (u < K_UNITS) {
+        const int g4 = u % (BN / 4), c = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *(u32x4*)&sK[buf][k_lds_row(4 * g4 + r) * KLD + 8 * c] = st[i][r];
+        if (!DELTA) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned a0 = st[i][0][e], a1 = st[i][1][e], a2 = st[i][2][e],
+                           a3 = st[i][3][e];
+            u32x2 lo, hi;
+            lo[0] = (a0 & 0xffffu) | (a1 << 16);
+            lo[1] = (a2 & 0xffffu) | (a3 << 16);
+            hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+            hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+            *(u32x2*)&sKt[buf][(8 * c + 2 * e) * TLD + 4 * g4] = lo;
+            *(u32x2*)&sKt[buf][(8 * c + 2 * e + 1) * TLD + 4 * g4] = hi;
+          }
+        }
+      } else if (u < UNITS) {
+        const int u2 = u - K_UNITS;
+        const int g4 = u2 % (BN / 4), c = u2 / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *(u32x4*)&sV[buf][k_lds_row(4 * g4 + r) * VLD + 8 * c] = st[i][r];
+      }
+    }
+    if (is_yat(VAR) && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = st_nk;
+  };
+
+  f32x16 accQ[KB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) accQ[i] = f32x16{};
+  float corr = 0.f;            // Yat: sum over the lane's keys of B' = bf16(g) - A
+  float sum0 = 0.f, sum1 = 0.f;  // Yat: sum A, sum B; s^tau: sum w (dp - D) log2(phi)
+  float dsum = 0.f;            // DELTA: sum over the lane's keys of w dp
+
+  // Scores of one tile -> packed gradient scores (pg) and the row sums.
+  auto scores = [&](auto mask_tag, int buf, int k0, u32x4* pg) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 sacc = {}, pacc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sK[buf][col * KLD + 16 * s + 8 * half]),
+                    qf[s], sacc);
+#pragma unroll
+    for (int s = 0; s < VS; ++s)
+      pacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sV[buf][col * VLD + 16 * s + 8 * half]),
+                    of[s], pacc);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // accumulator elements 8 s .. 8 s + 7: keys k0 + 16 s + 8 half + 0..7
+      const int k8 = 16 * s + 8 * half;
+      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
+      if (is_yat(VAR)) {
+        n0 = *(const f32x4*)&sNK[buf][k8];
+        n1 = *(const f32x4*)&sNK[buf][k8 + 4];
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float gv[2], av[2], bv[2], lv[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int e = 2 * e2 + o, r = 8 * s + e;
+          const float nkv = e < 4 ? n0[e] : n1[e - 4];
+          float wv;
+          pair_terms<VAR>(sacc[r], pacc[r], D, Z, nq + nkv, hc, wv, gv[o], av[o], bv[o], lv[o]);
+          if (MASK) {
+            const int kj = k0 + k8 + e;
+            const bool ok = my_q < p.Tq && kj < p.Tk && !(p.causal && kj > my_q);
+            wv = ok ? wv : 0.f;
+            gv[o] = ok ? gv[o] : 0.f;
+            av[o] = ok ? av[o] : 0.f;
+            bv[o] = ok ? bv[o] : 0.f;
+            lv[o] = ok ? lv[o] : 0.f;
+          }
+          if (DELTA) dsum = fmaf(wv, pacc[r], dsum);
+        }
+        if (DELTA) continue;
+        pg[s][e2] = pack_bf16(gv[0], gv[1]);
+        if (is_yat(VAR)) {
+          corr += (bf16_lo(pg[s][e2]) - av[0]) + (bf16_hi(pg[s][e2]) - av[1]);
+          sum0 += av[0] + av[1];
+          sum1 += bv[0] + bv[1];
+        } else if (VAR == kStau) {
+          sum0 += lv[0] + lv[1];
+        }
+      }
+    }
+  };
+  // dQ^T += K^T G^T (queries are the columns)
+  auto accumulate = [&](int buf, const u32x4* pg) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 bg = __builtin_bit_cast(bf16x8, pg[s]);
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        accQ[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sKt[buf][(32 * i + col) * TLD + 16 * s + 8 * half]),
+                         bg, accQ[i]);
+    }
+  };
+
+  // Staging as in attn_bwd_kv: tile t + 1 is written at the start of
+  // iteration t, tile t + 2 loaded after iteration t's scores.
+  if (n_tiles > 0) {
+    load(0);
+    store(0);
+    if (n_tiles > 1) load(BN);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = t * BN, buf = t & 1;
+    if (t + 1 < n_tiles) store(buf ^ 1);
+    const bool active = !(p.causal && k0 > qw + 31);
+    u32x4 pg[2];
+    if (active) {
+      const bool need_mask = (p.causal && k0 + BN - 1 > qw) || k0 + BN > p.Tk || qw + 32 > p.Tq;
+      if (need_mask) scores(std::true_type{}, buf, k0, pg);
+      else scores(std::false_type{}, buf, k0, pg);
+    }
+    if (t + 2 < n_tiles) load(k0 + 2 * BN);
+    if (active && !DELTA) accumulate(buf, pg);
+    __syncthreads();
+  }
+
+  if (DELTA) {
+    dsum = pair_sum(dsum);
+    if (my_q < p.Tq && half == 0) p.row_d[row_idx] = dsum;
+    return;
+  }
+
+  if (is_yat(VAR)) corr = pair_sum(corr);
+  if (my_q < p.Tq) {
+    unsigned short* dqrow = (unsigned short*)p.dq + (int64_t)b * p.qs[0] +
+                            (int64_t)h * p.qs[1] + (int64_t)my_q * p.qs[2];
+    const unsigned short* qrow = qbase + (int64_t)my_q * p.qs[2];
+    const float sc = is_yat(VAR) ? 1.f : 1.0f / sqrtf((float)DK);
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * i + 8 * g4 + 4 * half;
+        if (d0 < DK) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = accQ[i][4 * g4 + e] * sc;
+          if (is_yat(VAR)) {
+            const u32x2 qq = *(const u32x2*)&qrow[d0];
+            x[0] -= corr * bf16_lo(qq[0]);
+            x[1] -= corr * bf16_hi(qq[0]);
+            x[2] -= corr * bf16_lo(qq[1]);
+            x[3] -= corr * bf16_hi(qq[1]);
+          }
+          u32x2 o;
+          o[0] = pack_bf16(x[0], x[1]);
+          o[1] = pack_bf16(x[2], x[3]);
+          *(u32x2*)&dqrow[d0] = o;
+        }
+      }
+  }
+
+  // parameter sums of the workgroup: wave reduction, then the waves in order
+  if (VAR != kSoftmax && p.prm_part) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      sum0 += __shfl_xor(sum0, m, 64);
+      sum1 += __shfl_xor(sum1, m, 64);
+    }
+    if (lane == 0) {
+      sPrm[w][0] = sum0;
+      sPrm[w][1] = sum1;
+    }
+    __syncthreads();
+    if (tid < 2) {
+      double a = 0.0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) a += (double)sPrm[i][tid];
+      p.prm_part[(((int64_t)h * p.B + b) * n_qt + qt) * 2 + tid] = a;
+    }
+  }
+}
+
+template <int VAR, int DV>
+hipError_t launch_bwd_variant(const BwdProblem& p, hipStream_t stream) {
+  constexpr int DK = SFS_DK;
+  if (is_yat(VAR) && p.Tq > 0) {
+    hipLaunchKernelGGL(row_norms_bf16<DK>, dim3((p.Tk + 127) / 128, p.Hkv, p.B), dim3(256), 0,
+                       stream, (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk,
+                       p.nk);
+    hipLaunchKernelGGL(row_norms_bf16<DK>, dim3((p.Tq + 127) / 128, p.Hq, p.B), dim3(256), 0,
+                       stream, (const unsigned short*)p.q, p.qs[0], p.qs[1], p.qs[2], p.Hq, p.Tq,
+                       p.nq);
+  }
+  const unsigned n_q = (unsigned)((p.Tq + kBwdQRows - 1) / kBwdQRows) * (unsigned)p.B *
+                       (unsigned)p.Hq;
+  // D_i in fp32 from the weights (see attn_bwd_q)
+  if (p.Tq > 0)
+    hipLaunchKernelGGL((attn_bwd_q<VAR, DK, DV, true>), dim3(n_q), dim3(256), 0, stream, p);
+  const unsigned n_kv = (unsigned)((p.Tk + 127) / 128) * (unsigned)p.B * (unsigned)p.Hkv;
+  hipLaunchKernelGGL((attn_bwd_kv<VAR, DK, DV>), dim3(n_kv), dim3(256), 0, stream, p);
+  if (p.Tq == 0) return hipGetLastError();  // dk = dv = 0 written; no query rows
+  hipLaunchKernelGGL((attn_bwd_q<VAR, DK, DV, false>), dim3(n_q), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int VAR>
+hipError_t launch_bwd_dv(const BwdProblem& p, hipStream_t stream) {
+  switch (p.dv) {
+    case 16: return launch_bwd_variant<VAR, 16>(p, stream);
+    case 32: return launch_bwd_variant<VAR, 32>(p, stream);
+    case 64: return launch_bwd_variant<VAR, 64>(p, stream);
+    case 128: return launch_bwd_variant<VAR, 128>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t SFS_CAT(launch_bwd_bf16_dk, SFS_DK)(const BwdProblem& p, hipStream_t stream) {
+  switch (p.variant) {
+    case kSoftmax: return launch_bwd_dv<kSoftmax>(p, stream);
+    case kYat: return launch_bwd_dv<kYat>(p, stream);
+    case kStau: return launch_bwd_dv<kStau>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sfs

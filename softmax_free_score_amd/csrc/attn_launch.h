@@ -128,4 +128,50 @@ hipError_t launch_bf16_dk32(const Problem& p, hipStream_t stream);
 hipError_t launch_bf16_dk64(const Problem& p, hipStream_t stream);
 hipError_t launch_bf16_dk128(const Problem& p, hipStream_t stream);
 
+// Backward pass (bf16 storage).  Per query row i the API layer's first kernel
+// leaves the row normaliser the forward used: Yat 1 / (mass + 1e-9), s^tau
+// 1 / mass (0 if mass is 0), softmax L_i = max_score_i log2(e) + log2(mass_i)
+// (weights exp2(s log2(e) - L_i)); a first pass over the score tiles then
+// fills in D_i = sum_j w_ij dp_ij.
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  void* dq;          // strides of q
+  void* dk_;         // strides of k
+  void* dv_;         // strides of v
+  const float* b_raw;
+  const float* eps_raw;
+  const float* log_tau;
+  const float* mass;
+  const float* max_score;
+  float* db_raw;     // Yat; may be null
+  float* deps_raw;   // Yat; may be null
+  float* dlog_tau;   // s^tau; may be null
+  int64_t qs[3], ks[3], vs[3], os[3];  // os: strides of dout
+  int B, Hq, Hkv, Tq, Tk, dk, dv;
+  int variant;
+  int causal;
+  // workspace
+  float* nq;         // Yat: |q_i|^2 [B*Hq][nk_pitch(Tq)]
+  float* nk;         // Yat: |k_j|^2 [B*Hkv][nk_pitch(Tk)]
+  float* row_d;      // D_i = sum_j w_ij dp_ij [B*Hq][nk_pitch(Tq)] (0 past T_q)
+  float* row_z;      // row normaliser [B*Hq][nk_pitch(Tq)] (0 past T_q)
+  double* prm_part;  // [Hq][B][n_qt][2] per-workgroup sums for the parameter
+                     // gradients (n_qt = query tiles of the dq kernel)
+};
+// Query rows per workgroup of the dq kernel.
+constexpr int kBwdQRows = 128;
+
+// The row normaliser of every query row, and D cleared (before the passes).
+hipError_t launch_bwd_rows(const BwdProblem& p, hipStream_t stream);
+// dk, dv (key-tile kernel) and dq plus parameter sums (query-tile kernel).
+hipError_t launch_bwd_bf16_dk16(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_bf16_dk32(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_bf16_dk64(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_bf16_dk128(const BwdProblem& p, hipStream_t stream);
+// Per-head parameter gradients from the per-workgroup sums (fixed order).
+hipError_t launch_bwd_params(const BwdProblem& p, hipStream_t stream);
+
 }  // namespace sfs

@@ -171,3 +171,17 @@ def make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, dtype="bf16", causal=True, seed=0, q
     wl = Workload("custom", B, Hq, Hkv, Tq, Tk, dk, dv, dtype, causal, seed, qk_std, v_dist,
                   ("uniform", -1.0, 1.0), ("uniform", -3.0, 0.0), ("yat", "softmax", "stau"))
     return make_inputs(wl, tied=tied)
+
+
+def make_grad_out(inp: Inputs, seed_offset: int = 1000):
+    """The output gradient dL/dout for a backward on ``inp``: N(0, 1) of the
+    output's shape [B, Hq, Tq, dv], drawn from default_rng(seed + seed_offset)
+    and rounded to the storage dtype like q, k, v.  Returns (values as fp32,
+    bf16 bit patterns or None)."""
+    wl = inp.wl
+    rng = np.random.default_rng(wl.seed + seed_offset)
+    g = rng.standard_normal((wl.B, wl.Hq, wl.Tq, wl.dv), dtype=np.float32)
+    if wl.dtype == "bf16":
+        bits = bf16_bits(g)
+        return bf16_bits_to_f32(bits), bits
+    return g, None

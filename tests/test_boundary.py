@@ -226,3 +226,57 @@ def test_telemetry_workspace_bytes():
     nk = 2 * 2 * 128 * 4                                              # |k|^2 rows, pitch 128
     assert lib.attn_telemetry_workspace_bytes(ctypes.byref(d), attn.ATTN_YAT) == \
         (nk + 255) // 256 * 256 + tau_bytes
+
+
+DO, DQ, DKG, DVG, GB, GE, GT = (0x200000 + 0x10000 * i for i in range(7))
+
+
+def call_bwd(d, variant=attn.ATTN_SOFTMAX, causal=1, q=A, k=K, v=V, dout=DO, mass=M,
+             mx=X, dq=DQ, dk=DKG, dv=DVG, b=BR, e=ER, lt=LT, gb=GB, ge=GE, gt=GT, ws=W,
+             ws_bytes=1 << 30):
+    lib = attn.load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.attn_bwd(ctypes.byref(d) if d is not None else None, p(q), p(k), p(v),
+                        p(dout), variant, p(b), p(e), p(lt), causal, p(mass), p(mx), p(dq),
+                        p(dk), p(dv), p(gb), p(ge), p(gt), p(ws), ws_bytes, None)
+
+
+def test_bwd_validation():
+    assert call_bwd(desc()) == ERR_HIP                               # valid, no device
+    assert call_bwd(None) == ERR_NULL
+    assert call_bwd(desc(dtype=attn.ATTN_F32)) == ERR_UNSUP
+    for kw in ("q", "k", "v", "dout", "dq", "dk", "dv", "mass"):
+        assert call_bwd(desc(), **{kw: 0}) == ERR_NULL, kw
+    assert call_bwd(desc(), mx=0) == ERR_NULL                        # softmax needs max_score
+    assert call_bwd(desc(), variant=attn.ATTN_YAT, mx=0) == ERR_HIP  # Yat does not
+    assert call_bwd(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
+    assert call_bwd(desc(), variant=attn.ATTN_STAU, lt=0) == ERR_PARAM
+    # parameter gradients are optional
+    assert call_bwd(desc(), variant=attn.ATTN_YAT, gb=0, ge=0) == ERR_HIP
+    assert call_bwd(desc(), dq=DQ + 8) == ERR_UNSUP                  # misaligned
+    assert call_bwd(desc(), variant=attn.ATTN_YAT, gb=GB + 2) == ERR_UNSUP
+    assert call_bwd(desc(Tq=64, Tk=32)) == ERR_SHAPE                 # causal needs Tq == Tk
+    assert call_bwd(desc(dk=48)) == ERR_UNSUP
+    assert call_bwd(desc(), ws=0) == ERR_WS
+    assert call_bwd(desc(), ws_bytes=16) == ERR_WS
+    # empty problems: B == 0 enqueues nothing; Tq == 0 still writes dk = dv = 0
+    assert call_bwd(desc(B=0)) == OK
+    assert call_bwd(desc(Tq=0), causal=0) == ERR_HIP
+    assert call_bwd(desc(Tq=0), causal=0, dk=0) == ERR_NULL
+
+
+def test_bwd_workspace_bytes():
+    lib = attn.load_library()
+    d = desc(B=2, Hq=4, Hkv=2, Tq=130, Tk=100, dk=64, dv=64)
+    rows = 2 * 4 * 192 * 4                                    # Tq pitch 192 (multiple of 64)
+    n_qt = 2                                                  # 130 rows / 128
+    prm = 4 * 2 * n_qt * 2 * 8
+    al = lambda x: (x + 255) // 256 * 256
+    ws = lambda v: lib.attn_bwd_workspace_bytes(ctypes.byref(d), v)
+    assert ws(attn.ATTN_SOFTMAX) == 2 * al(rows)
+    assert ws(attn.ATTN_STAU) == 2 * al(rows) + prm
+    nk = 2 * 2 * 128 * 4
+    assert ws(attn.ATTN_YAT) == al(nk) + 3 * al(rows) + prm
+    assert ws(7) == 0
+    d.dtype = attn.ATTN_F32
+    assert ws(attn.ATTN_SOFTMAX) == 0

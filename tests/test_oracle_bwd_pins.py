@@ -180,3 +180,27 @@ def test_single_key_has_no_score_gradient():
         g = bwd(x, dout, variant, False)
         assert np.abs(g["dq"]).max() < 1e-15 and np.abs(g["dk"]).max() < 1e-15
         np.testing.assert_allclose(g["dv"], dout, rtol=1e-14)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_error_scales_bound_the_gradients(variant, causal):
+    """The error scales replace every factor by its absolute value and the
+    difference dw - D by |dw| + |D|, so by the triangle inequality each one
+    bounds its gradient elementwise; and with one allowed key per row the q
+    and k gradients vanish while their scales do not."""
+    x, dout = make(38, 2, 4, 2, 9, 9, 5, 3, scale=1.3)
+    g = oracle.attn_bwd_np(x["q"], x["k"], x["v"], dout, variant, b_raw=x["b_raw"],
+                           eps_raw=x["eps_raw"], log_tau=x["log_tau"], causal=causal,
+                           return_abs=True)
+    for n in ("dq", "dk", "dv", "db_raw", "deps_raw", "dlog_tau"):
+        assert np.all(np.abs(g[n]) <= g[n + "_abs"] * (1 + 1e-12) + 1e-300), n
+    x, dout = make(39, 1, 2, 2, 4, 1, 5, 3)
+    g = oracle.attn_bwd_np(x["q"], x["k"], x["v"], dout, variant, b_raw=x["b_raw"],
+                           eps_raw=x["eps_raw"], log_tau=x["log_tau"], return_abs=True)
+    # softmax and s^tau: w = 1 exactly; Yat: w = kappa / (kappa + 1e-9), so the
+    # gradient is that 1e-9 / (kappa + 1e-9) fraction of the terms
+    bound = 1e-4 if variant == "yat" else 1e-12
+    assert np.abs(g["dq"]).max() < bound * g["dq_abs"].max()
+    assert np.abs(g["dk"]).max() < bound * g["dk_abs"].max()
+    assert g["dq_abs"].min() > 0
