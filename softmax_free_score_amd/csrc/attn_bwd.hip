@@ -27,8 +27,8 @@
 //
 // Design (gfx950 / CDNA4, wave64, v_mfma_f32_32x32x16_bf16 throughout):
 //   * Two kernels, no atomics: attn_bwd_kv owns 128 keys of one (b, kv head)
-//     per workgroup (32 per wave, their k and v rows in registers) and streams
-//     32-query tiles of every query head of the group; attn_bwd_q owns 128
+//     per workgroup (32 per pair of waves, their k and v rows in registers)
+//     and streams 32-query tiles of every query head of the group; attn_bwd_q owns 128
 //     query rows of one (b, h) (32 per wave) and streams 32-key tiles.  Each
 //     recomputes the score tile (and dp) it needs, so both the score and the
 //     dp products are taken twice; in exchange every output is written once,
@@ -129,29 +129,47 @@ __device__ __forceinline__ void pair_terms(float sd, float dp, float D, float Z,
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves x 32 keys; 32-query tiles of every query head of the group.
+// dK, dV: 8 waves in 4 pairs; pair p owns keys k0 + 32 p .. k0 + 32 p + 31 of
+// one (b, kv head) and streams 32-query tiles of every query head of the
+// group.  Wave p ("A") holds the pair's key rows and the dV^T accumulator;
+// wave p + 4 ("B") holds the value rows and the dK^T accumulator.  Each
+// keeps one row fragment and one accumulator, which is what lets two waves
+// share a SIMD without spilling, and each issues 16 of a tile's 32 MFMAs.
+// The two are pipelined one tile apart, one barrier per tile:
+//
+//   iteration t:  A: weights of tile t from S_t (its registers), dV^T += dO^T P,
+//                    S_{t+1} = Q_{t+1} K^T -> registers and LDS
+//                 B: dP_t = dO_t V^T, S_t <- LDS, gradient scores, dK^T += Q^T G
+//
+// so on each SIMD one wave's matrix-core work overlaps the other's vector
+// work.  Tiles live in three LDS stages: tile t is read in iteration t (and
+// its Q rows already in t - 1), tile t + 2 is written in iteration t from
+// registers loaded in iteration t - 1.
 template <int VAR, int DK, int DV>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
                           amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv(BwdProblem p) {
-  constexpr int NW = 4, NT = 64 * NW, BK = 32 * NW, BQ = 32;
-  constexpr int KS = DK / 16, VS = DV / 16;
+  constexpr int NP = 4, NT = 128 * NP, BK = 32 * NP, BQ = 32, NS = 3;
+  constexpr int KS = DK / 16, VS = DV / 16, FS = KS > VS ? KS : VS;
   constexpr int DKP = DK < 32 ? 32 : DK, DVP = DV < 32 ? 32 : DV;
-  constexpr int KB = DKP / 32, VB = DVP / 32;
+  constexpr int KB = DKP / 32, VB = DVP / 32, AB = KB > VB ? KB : VB;
   constexpr int QLD = DK + 8, OLD = DV + 8, TLD = BQ + 8;
   constexpr int Q_UNITS = (BQ / 4) * (DK / 8), O_UNITS = (BQ / 4) * (DV / 8);
   constexpr int UNITS = Q_UNITS + O_UNITS;
   constexpr int PER_T = (UNITS + NT - 1) / NT;
 
-  __shared__ __attribute__((aligned(16))) unsigned short sQ[2][BQ * QLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sQt[2][DKP * TLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sO[2][BQ * OLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sOt[2][DVP * TLD];
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sZ[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sNQ[2][BQ];
+  __shared__ __attribute__((aligned(16))) unsigned short sQ[NS][BQ * QLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sQt[NS][DKP * TLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sO[NS][BQ * OLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sOt[NS][DVP * TLD];
+  __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
+  __shared__ __attribute__((aligned(16))) float sZ[NS][BQ];
+  __shared__ __attribute__((aligned(16))) float sNQ[NS][BQ];
+  __shared__ f32x4 sS[2][NP][4][64];  // score tiles, in A's register layout
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
+  const bool is_a = w < NP;
+  const int pr = w & (NP - 1);
   // Workgroup -> (key tile, batch, kv head), heads fastest.  With a causal
   // mask the first key tiles have the most queries and go first.
   const int nbh = p.B * p.Hkv;
@@ -159,32 +177,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   const int bh = blockIdx.x - kt * nbh;
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   const int g = p.Hq / p.Hkv;
-  const int k0 = kt * BK, kw = k0 + 32 * w, my_k = kw + col;
+  const int k0 = kt * BK, kw = k0 + 32 * pr, my_k = kw + col;
 
   const unsigned short* kbase =
       (const unsigned short*)p.k + (int64_t)b * p.ks[0] + (int64_t)hk * p.ks[1];
   const unsigned short* vbase =
       (const unsigned short*)p.v + (int64_t)b * p.vs[0] + (int64_t)hk * p.vs[1];
-  const uint32_t k_bytes = slice_bytes(p.Tk, p.ks[2], DK);
-  const uint32_t v_bytes = slice_bytes(p.Tk, p.vs[2], DV);
   const uint32_t q_bytes = slice_bytes(p.Tq, p.qs[2], DK);
   const uint32_t o_bytes = slice_bytes(p.Tq, p.os[2], DV);
   const int qst = (int)p.qs[2], ost = (int)p.os[2];
 
-  // This lane's key and value rows: the B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[KS], vf[VS];
+  // A: this lane's key row, the B operand of S = Q K^T; B: its value row,
+  // the B operand of dP = dO V^T.
+  bf16x8 frag[FS];
   {
-    const rsrc_t rk = make_rsrc(kbase, k_bytes);
-    const rsrc_t rv = make_rsrc(vbase, v_bytes);
-    const uint32_t ko = my_k < p.Tk ? (uint32_t)(((int64_t)my_k * p.ks[2] + 8 * half) * 2)
-                                    : k_bytes;
-    const uint32_t vo = my_k < p.Tk ? (uint32_t)(((int64_t)my_k * p.vs[2] + 8 * half) * 2)
-                                    : v_bytes;
+    const uint32_t k_bytes = slice_bytes(p.Tk, p.ks[2], DK);
+    const uint32_t v_bytes = slice_bytes(p.Tk, p.vs[2], DV);
+    const rsrc_t r = is_a ? make_rsrc(kbase, k_bytes) : make_rsrc(vbase, v_bytes);
+    const int64_t rs = is_a ? p.ks[2] : p.vs[2];
+    const uint32_t lim = is_a ? k_bytes : v_bytes;
+    const uint32_t off = my_k < p.Tk ? (uint32_t)((my_k * rs + 8 * half) * 2) : lim;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = __builtin_bit_cast(bf16x8, ld128(rk, ko + 32 * s));
-#pragma unroll
-    for (int s = 0; s < VS; ++s) vf[s] = __builtin_bit_cast(bf16x8, ld128(rv, vo + 32 * s));
+    for (int s = 0; s < FS; ++s)
+      if (s < (is_a ? KS : VS)) frag[s] = __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s));
   }
+
   const int n_qt = (p.Tq + BQ - 1) / BQ;
   const int qt0 = p.causal ? k0 / BQ : 0;  // causal: T_q == T_k, so qt0 < n_qt
   const int per_head = n_qt - qt0;
@@ -194,12 +211,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   if (is_yat(VAR) && n_it > 0 && my_k < p.Tk)
     nk = p.nk[((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) + my_k];
 
-  // Staging registers for the next query tile.
+  // Tile it covers query head hk * g + it / per_head, query tile
+  // qt0 + it % per_head; the loops below step these instead of dividing.
+  struct Pos {
+    int gi, qt;
+  };
+  auto advance = [&](Pos& x) {
+    if (++x.qt == n_qt) {
+      x.qt = qt0;
+      ++x.gi;
+    }
+  };
+
+  // Staging registers for a query tile.
   u32x4 st[PER_T][4];
   float st_d = 0.f, st_z = 0.f, st_nq = 0.f;
-  auto load = [&](int it) {
-    const int gi = it / per_head, qt = qt0 + it - gi * per_head;
-    const int h = hk * g + gi, qb = qt * BQ;
+  auto load = [&](Pos x) {
+    const int h = hk * g + x.gi, qb = x.qt * BQ;
     const rsrc_t rq = make_rsrc((const unsigned short*)p.q + (int64_t)b * p.qs[0] +
                                     (int64_t)h * p.qs[1], q_bytes);
     const rsrc_t ro = make_rsrc((const unsigned short*)p.dout + (int64_t)b * p.os[0] +
@@ -249,54 +277,59 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
       *(u32x2*)&Tr[(8 * c + 2 * e + 1) * TLD + 4 * g4] = hi;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int u = tid + i * NT;
       if (u < Q_UNITS) {
-        put(st[i], u % (BQ / 4), u / (BQ / 4), sQ[buf], QLD, sQt[buf]);
+        put(st[i], u % (BQ / 4), u / (BQ / 4), sQ[slot], QLD, sQt[slot]);
       } else if (u < UNITS) {
         const int u2 = u - Q_UNITS;
-        put(st[i], u2 % (BQ / 4), u2 / (BQ / 4), sO[buf], OLD, sOt[buf]);
+        put(st[i], u2 % (BQ / 4), u2 / (BQ / 4), sO[slot], OLD, sOt[slot]);
       }
     }
     if (tid < BQ) {
-      sD[buf][tid] = st_d;
-      sZ[buf][tid] = st_z;
-      sNQ[buf][tid] = st_nq;
+      sD[slot][tid] = st_d;
+      sZ[slot][tid] = st_z;
+      sNQ[slot][tid] = st_nq;
     }
   };
-
-  f32x16 accK[KB], accV[VB];
-#pragma unroll
-  for (int i = 0; i < KB; ++i) accK[i] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < VB; ++i) accV[i] = f32x16{};
-  float corr = 0.f;  // Yat: sum over the lane's queries of B' = bf16(g) - A
-  HeadC hc{};
-
-  // Scores of one tile -> packed weights (pw) and gradient scores (pg).
-  auto scores = [&](auto mask_tag, int buf, int qb, u32x4* pw, u32x4* pg) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 sacc = {}, pacc = {};
+  // A: S = Q K^T of the tile in `slot`, kept in registers and handed to B.
+  auto scores = [&](int slot, int ss, f32x16& sacc) {
+    sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQ[buf][col * QLD + 16 * s + 8 * half]),
-                    kf[s], sacc);
+      sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQ[slot][col * QLD + 16 * s + 8 * half]),
+                    frag[s], sacc);
 #pragma unroll
-    for (int s = 0; s < VS; ++s)
-      pacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sO[buf][col * OLD + 16 * s + 8 * half]),
-                    vf[s], pacc);
+    for (int m = 0; m < 4; ++m)
+      sS[ss][pr][m][lane] = f32x4{sacc[4 * m], sacc[4 * m + 1], sacc[4 * m + 2], sacc[4 * m + 3]};
+  };
+  // a tile whose every query precedes every key of this pair: nothing to do
+  auto active = [&](int qt) { return !(p.causal && qt * BQ + BQ - 1 < kw); };
+
+  // A: dV^T; B: dK^T (rows are value / key columns, the keys are the columns)
+  f32x16 acc[AB];
+#pragma unroll
+  for (int i = 0; i < AB; ++i) acc[i] = f32x16{};
+  float corr = 0.f;  // B, Yat: sum over the lane's queries of B' = bf16(g) - A
+  HeadC hc{};
+
+  // The per-pair terms of one tile from S (sacc) and, in B, dP (pacc); then
+  // A: dV^T += dO^T P, B: dK^T += Q^T G.
+  auto terms = [&](auto mask_tag, int slot, int qb, const f32x16& sacc, const f32x16& pacc) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    u32x4 pk[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // accumulator elements 8 s .. 8 s + 7: queries qb + 16 s + 8 half + 0..7
       const int q8 = 16 * s + 8 * half;
-      const f32x4 d0 = *(const f32x4*)&sD[buf][q8], d1 = *(const f32x4*)&sD[buf][q8 + 4];
-      const f32x4 z0 = *(const f32x4*)&sZ[buf][q8], z1 = *(const f32x4*)&sZ[buf][q8 + 4];
+      const f32x4 d0 = *(const f32x4*)&sD[slot][q8], d1 = *(const f32x4*)&sD[slot][q8 + 4];
+      const f32x4 z0 = *(const f32x4*)&sZ[slot][q8], z1 = *(const f32x4*)&sZ[slot][q8 + 4];
       f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
       if (is_yat(VAR)) {
-        n0 = *(const f32x4*)&sNQ[buf][q8];
-        n1 = *(const f32x4*)&sNQ[buf][q8 + 4];
+        n0 = *(const f32x4*)&sNQ[slot][q8];
+        n1 = *(const f32x4*)&sNQ[slot][q8 + 4];
       }
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -317,103 +350,139 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
             av[o] = ok ? av[o] : 0.f;
           }
         }
-        pw[s][e2] = pack_bf16(wv[0], wv[1]);
-        pg[s][e2] = pack_bf16(gv[0], gv[1]);
-        if (is_yat(VAR)) corr += (bf16_lo(pg[s][e2]) - av[0]) + (bf16_hi(pg[s][e2]) - av[1]);
+        if (is_a) {
+          pk[s][e2] = pack_bf16(wv[0], wv[1]);
+        } else {
+          pk[s][e2] = pack_bf16(gv[0], gv[1]);
+          if (is_yat(VAR)) corr += (bf16_lo(pk[s][e2]) - av[0]) + (bf16_hi(pk[s][e2]) - av[1]);
+        }
       }
     }
-  };
-  // dV^T += dO^T P, dK^T += Q^T G (keys are the columns)
-  auto accumulate = [&](int buf, const u32x4* pw, const u32x4* pg) {
+    const unsigned short* T = is_a ? sOt[slot] : sQt[slot];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, pw[s]);
-      const bf16x8 bg = __builtin_bit_cast(bf16x8, pg[s]);
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, pk[s]);
 #pragma unroll
-      for (int i = 0; i < VB; ++i)
-        accV[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sOt[buf][(32 * i + col) * TLD + 16 * s + 8 * half]),
-                         bw, accV[i]);
-#pragma unroll
-      for (int i = 0; i < KB; ++i)
-        accK[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQt[buf][(32 * i + col) * TLD + 16 * s + 8 * half]),
-                         bg, accK[i]);
+      for (int i = 0; i < AB; ++i)
+        if (i < (is_a ? VB : KB))
+          acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&T[(32 * i + col) * TLD + 16 * s + 8 * half]),
+                          bop, acc[i]);
     }
   };
 
-  // Stage it is written at the start of iteration it - 1 (the prologue for
-  // it = 0, 1) from registers loaded during iteration it - 2, after that
-  // iteration's scores, so that the staging registers and the score tiles
-  // are not live at the same time.
+  // Prologue: tiles 0 and 1 into their stages, tile 2 into registers, S_0.
+  Pos cur{0, qt0};       // tile it
+  Pos nxt = cur;         // tile it + 1
+  Pos ld = cur;          // next tile to load
+  f32x16 s_cur = {};     // A: S of tile it
   if (n_it > 0) {
-    load(0);
+    load(ld);
     store(0);
-    if (n_it > 1) load(1);
+    advance(ld);
+    if (n_it > 1) {
+      load(ld);
+      store(1);
+      advance(ld);
+    }
+    if (n_it > 2) {
+      load(ld);
+      advance(ld);
+    }
   }
+  advance(nxt);
+  __syncthreads();
+  if (n_it > 0 && is_a && active(cur.qt)) scores(0, 0, s_cur);
   __syncthreads();
 
   for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    // stage buf ^ 1 was last read in iteration it - 1, finished by all waves
-    if (it + 1 < n_it) store(buf ^ 1);
-    const int gi = it / per_head, qt = qt0 + it - gi * per_head;
-    const int qb = qt * BQ;
-    if (it == 0 || qt == qt0) hc = head_consts<VAR, DK>(p, hk * g + gi);
-    // a tile whose every query precedes every key of this wave: nothing to do
-    const bool active = !(p.causal && qb + BQ - 1 < kw);
-    u32x4 pw[2], pg[2];
-    if (active) {
-      const bool need_mask = (p.causal && qb < kw + 32) || qb + BQ > p.Tq;
-      if (need_mask) scores(std::true_type{}, buf, qb, pw, pg);
-      else scores(std::false_type{}, buf, qb, pw, pg);
+    const int slot = it % NS;
+    // stage (it + 2) % 3 was last read in iteration it - 1
+    if (it + 2 < n_it) store((it + 2) % NS);
+    if (it + 3 < n_it) {
+      load(ld);
+      advance(ld);
     }
-    if (it + 2 < n_it) load(it + 2);
-    if (active) accumulate(buf, pw, pg);
+    const int qb = cur.qt * BQ;
+    if (it == 0 || cur.qt == qt0) hc = head_consts<VAR, DK>(p, hk * g + cur.gi);
+    const bool act = active(cur.qt);
+    const bool need_mask = (p.causal && qb < kw + 32) || qb + BQ > p.Tq;
+    if (is_a) {
+      if (act) {
+        const f32x16 none = {};
+        if (need_mask) terms(std::true_type{}, slot, qb, s_cur, none);
+        else terms(std::false_type{}, slot, qb, s_cur, none);
+      }
+      if (it + 1 < n_it && active(nxt.qt)) scores((it + 1) % NS, (it + 1) & 1, s_cur);
+    } else if (act) {
+      f32x16 pacc = {};
+#pragma unroll
+      for (int s = 0; s < VS; ++s)
+        pacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sO[slot][col * OLD + 16 * s + 8 * half]),
+                      frag[s], pacc);
+      f32x16 sacc;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 x = sS[it & 1][pr][m][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[4 * m + e] = x[e];
+      }
+      if (need_mask) terms(std::true_type{}, slot, qb, sacc, pacc);
+      else terms(std::false_type{}, slot, qb, sacc, pacc);
+    }
+    cur = nxt;
+    advance(nxt);
     __syncthreads();
   }
 
-  if (is_yat(VAR)) corr = pair_sum(corr);
   if (my_k < p.Tk) {
-    unsigned short* dkrow = (unsigned short*)p.dk_ + (int64_t)b * p.ks[0] +
-                            (int64_t)hk * p.ks[1] + (int64_t)my_k * p.ks[2];
-    unsigned short* dvrow = (unsigned short*)p.dv_ + (int64_t)b * p.vs[0] +
-                            (int64_t)hk * p.vs[1] + (int64_t)my_k * p.vs[2];
-    const unsigned short* krow = kbase + (int64_t)my_k * p.ks[2];
-    const float sc = is_yat(VAR) ? 1.f : 1.0f / sqrtf((float)DK);
-    // accumulator element 4 g4 + e of block i: row 32 i + 8 g4 + 4 half + e
+    if (is_a) {
+      unsigned short* dvrow = (unsigned short*)p.dv_ + (int64_t)b * p.vs[0] +
+                              (int64_t)hk * p.vs[1] + (int64_t)my_k * p.vs[2];
+      // accumulator element 4 g4 + e of block i: row 32 i + 8 g4 + 4 half + e
 #pragma unroll
-    for (int i = 0; i < KB; ++i)
+      for (int i = 0; i < VB; ++i)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * i + 8 * g4 + 4 * half;
-        if (d0 < DK) {
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = accK[i][4 * g4 + e] * sc;
-          if (is_yat(VAR)) {
-            const u32x2 kk = *(const u32x2*)&krow[d0];
-            x[0] -= corr * bf16_lo(kk[0]);
-            x[1] -= corr * bf16_hi(kk[0]);
-            x[2] -= corr * bf16_lo(kk[1]);
-            x[3] -= corr * bf16_hi(kk[1]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * i + 8 * g4 + 4 * half;
+          if (d0 < DV) {
+            u32x2 o;
+            o[0] = pack_bf16(acc[i][4 * g4], acc[i][4 * g4 + 1]);
+            o[1] = pack_bf16(acc[i][4 * g4 + 2], acc[i][4 * g4 + 3]);
+            *(u32x2*)&dvrow[d0] = o;
           }
-          u32x2 o;
-          o[0] = pack_bf16(x[0], x[1]);
-          o[1] = pack_bf16(x[2], x[3]);
-          *(u32x2*)&dkrow[d0] = o;
         }
-      }
+    }
+  }
+  if (!is_a) {
+    if (is_yat(VAR)) corr = pair_sum(corr);
+    if (my_k < p.Tk) {
+      unsigned short* dkrow = (unsigned short*)p.dk_ + (int64_t)b * p.ks[0] +
+                              (int64_t)hk * p.ks[1] + (int64_t)my_k * p.ks[2];
+      const unsigned short* krow = kbase + (int64_t)my_k * p.ks[2];
+      const float sc = is_yat(VAR) ? 1.f : 1.0f / sqrtf((float)DK);
 #pragma unroll
-    for (int i = 0; i < VB; ++i)
+      for (int i = 0; i < KB; ++i)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * i + 8 * g4 + 4 * half;
-        if (d0 < DV) {
-          u32x2 o;
-          o[0] = pack_bf16(accV[i][4 * g4], accV[i][4 * g4 + 1]);
-          o[1] = pack_bf16(accV[i][4 * g4 + 2], accV[i][4 * g4 + 3]);
-          *(u32x2*)&dvrow[d0] = o;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * i + 8 * g4 + 4 * half;
+          if (d0 < DK) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[i][4 * g4 + e] * sc;
+            if (is_yat(VAR)) {
+              const u32x2 kk = *(const u32x2*)&krow[d0];
+              x[0] -= corr * bf16_lo(kk[0]);
+              x[1] -= corr * bf16_hi(kk[0]);
+              x[2] -= corr * bf16_lo(kk[1]);
+              x[3] -= corr * bf16_hi(kk[1]);
+            }
+            u32x2 o;
+            o[0] = pack_bf16(x[0], x[1]);
+            o[1] = pack_bf16(x[2], x[3]);
+            *(u32x2*)&dkrow[d0] = o;
+          }
         }
-      }
+    }
   }
 }
 
@@ -732,7 +801,7 @@ hipError_t launch_bwd_variant(const BwdProblem& p, hipStream_t stream) {
   if (p.Tq > 0)
     hipLaunchKernelGGL((attn_bwd_q<VAR, DK, DV, true>), dim3(n_q), dim3(256), 0, stream, p);
   const unsigned n_kv = (unsigned)((p.Tk + 127) / 128) * (unsigned)p.B * (unsigned)p.Hkv;
-  hipLaunchKernelGGL((attn_bwd_kv<VAR, DK, DV>), dim3(n_kv), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_bwd_kv<VAR, DK, DV>), dim3(n_kv), dim3(512), 0, stream, p);
   if (p.Tq == 0) return hipGetLastError();  // dk = dv = 0 written; no query rows
   hipLaunchKernelGGL((attn_bwd_q<VAR, DK, DV, false>), dim3(n_q), dim3(256), 0, stream, p);
   return hipGetLastError();
