@@ -44,13 +44,18 @@ def alg_bytes(wl) -> float:
     return float(q + kv + o + stats)
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "softmax_free_score_amd", "csrc", "attn_bf16.hip")
+# sources the fused forward kernel is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "softmax_free_score_amd", "csrc", f)
+                  for f in ("attn_bf16.hip", "bf16_common.h", "attn_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload: str, variant: str):
@@ -116,7 +121,9 @@ def cpu_baseline(inp, variant, target_s=25.0):
     flops = pairs_of(rows) * 2.0 * (wl.dk + wl.dv)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{variant}, 1 query row in {stride} of {wl.name} ({len(rows)} rows, "
+            "sample": f"{variant}, "
+                      + ("every query row" if stride == 1 else f"1 query row in {stride}")
+                      + f" of {wl.name} ({len(rows)} rows, "
                       f"{pairs_of(rows):.3e} allowed pairs) in {dt:.1f} s, fp64 C loops, OpenMP"}
 
 
