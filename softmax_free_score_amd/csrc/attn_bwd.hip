@@ -50,9 +50,12 @@
 //   * Yat |q|^2 and |k|^2 come from the same MFMA pre-pass as the forward's,
 //     so d2 = |q|^2 + |k|^2 - 2 q.k cancels to exactly 0 for a key equal to
 //     its query.
-//   * Parameter gradients: attn_bwd_q sums A and B (Yat) or
+//   * Parameter gradients: attn_bwd_q sums A/2 and B/2 (Yat) or
 //     w (dp - D) log2(phi) (s^tau) per workgroup; a last kernel adds the
 //     workgroup sums per head in a fixed order.
+//   * Yat carries g/2 = A/2 (1 + u/den) and A/2 = (dp - D) Z u / den, u = q.k
+//     + b, which needs neither kappa nor the factor 2 per pair; outputs and
+//     sums are doubled at the end (exact in binary floating point).
 #include "bf16_common.h"
 
 #include <type_traits>
@@ -87,28 +90,16 @@ __device__ __forceinline__ HeadC head_consts(const BwdProblem& p, int h) {
   return c;
 }
 
-// One pair: from sd = q.k, dp = dout.v, the row's D and normaliser Z (softmax:
-// L, the log2 normaliser) and, for Yat, nqk = |q|^2 + |k|^2, the weight w, the
-// gradient score g (before the 1/sqrt(d_k) of softmax and s^tau) and the
-// terms of the Yat correction and parameter sums (a, bc) or the s^tau one (lt).
+// The forward's weight of one pair from sd = q.k, the row normaliser Z
+// (softmax: L, the log2 normaliser) and, for Yat, nqk = |q|^2 + |k|^2.
 template <int VAR>
-__device__ __forceinline__ void pair_terms(float sd, float dp, float D, float Z, float nqk,
-                                           const HeadC& hc, float& w, float& g, float& a,
-                                           float& bc, float& lt) {
+__device__ __forceinline__ float pair_weight(float sd, float Z, float nqk, const HeadC& hc) {
   if constexpr (is_yat(VAR)) {
     const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
     const float u = sd + hc.bias;
-    const float kap = u * u * rden;
-    w = kap * Z;
-    const float t = 2.f * (dp - D) * Z * rden;
-    a = t * u;
-    bc = t * kap;
-    g = a + bc;
-    lt = 0.f;
+    return u * (u * rden) * Z;
   } else if constexpr (VAR == kSoftmax) {
-    w = __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
-    g = w * (dp - D);
-    a = bc = lt = 0.f;
+    return __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
   } else {
     const float s = sd * hc.scale;
     // softplus as the forward takes it: max(s, 0) + log1p(e), e = exp(-|s|),
@@ -117,14 +108,44 @@ __device__ __forceinline__ void pair_terms(float sd, float dp, float D, float Z,
     const float u1 = 1.f + e;
     const float c = (u1 - 1.f) - e;
     const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
+    return __builtin_amdgcn_exp2f(hc.tau * __builtin_amdgcn_logf(sp + 1e-6f)) * Z;
+  }
+}
+
+// The gradient score of one pair from sd, dp = dout.v, the row's D and Z and
+// (Yat) nqk, before the 1/sqrt(d_k) of softmax and s^tau, plus the terms of
+// the Yat correction (a) and of the s^tau parameter sum (lt).
+//   Yat:   returns g/2 and a = A/2 (the kernels double the results; exact):
+//          with r = 1/den, u = q.k + b:  A/2 = (dp - D) Z u r,
+//          g/2 = A/2 + B/2 = A/2 (1 + u r)  since B/A = kappa/u = u r.
+//   softmax: g = w (dp - D);  s^tau: g = w (dp - D) tau sigmoid(s) / phi,
+//          lt = w (dp - D) log2(phi).
+template <int VAR>
+__device__ __forceinline__ void pair_grad(float sd, float dp, float D, float Z, float nqk,
+                                          const HeadC& hc, float& g, float& a, float& lt) {
+  if constexpr (is_yat(VAR)) {
+    const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
+    const float ur = (sd + hc.bias) * rden;
+    a = (dp - D) * Z * (sd + hc.bias) * rden;
+    g = fmaf(a, ur, a);
+    lt = 0.f;
+  } else if constexpr (VAR == kSoftmax) {
+    g = __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z)) * (dp - D);
+    a = lt = 0.f;
+  } else {
+    const float s = sd * hc.scale;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+    const float u1 = 1.f + e;
+    const float c = (u1 - 1.f) - e;
+    const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
     const float phi = sp + 1e-6f;
     const float lp = __builtin_amdgcn_logf(phi);  // log2(phi)
-    w = __builtin_amdgcn_exp2f(hc.tau * lp) * Z;
+    const float w = __builtin_amdgcn_exp2f(hc.tau * lp) * Z;
     const float sig = (s >= 0.f ? 1.f : e) * __builtin_amdgcn_rcpf(u1);  // sigmoid(s)
     const float dw = w * (dp - D);
     g = dw * hc.tau * sig * __builtin_amdgcn_rcpf(phi);
     lt = dw * lp;
-    a = bc = 0.f;
+    a = 0.f;
   }
 }
 
@@ -312,59 +333,65 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   f32x16 acc[AB];
 #pragma unroll
   for (int i = 0; i < AB; ++i) acc[i] = f32x16{};
-  float corr = 0.f;  // B, Yat: sum over the lane's queries of B' = bf16(g) - A
+  float corr = 0.f;  // B, Yat: sum over the lane's queries of B'/2 = bf16(g/2) - A/2
   HeadC hc{};
 
   // The per-pair terms of one tile from S (sacc) and, in B, dP (pacc); then
-  // A: dV^T += dO^T P, B: dK^T += Q^T G.
-  auto terms = [&](auto mask_tag, int slot, int qb, const f32x16& sacc, const f32x16& pacc) {
+  // A: dV^T += dO^T P, B: dK^T += Q^T G.  ROLE_A is the wave's role, so each
+  // wave computes only its own terms.
+  auto terms = [&](auto mask_tag, auto role_tag, int slot, int qb, const f32x16& sacc,
+                   const f32x16& pacc) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool ROLE_A = decltype(role_tag)::value;
     u32x4 pk[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // accumulator elements 8 s .. 8 s + 7: queries qb + 16 s + 8 half + 0..7
       const int q8 = 16 * s + 8 * half;
-      const f32x4 d0 = *(const f32x4*)&sD[slot][q8], d1 = *(const f32x4*)&sD[slot][q8 + 4];
+      f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, n0 = d0, n1 = d0;
+      if (!ROLE_A) {
+        d0 = *(const f32x4*)&sD[slot][q8];
+        d1 = *(const f32x4*)&sD[slot][q8 + 4];
+      }
       const f32x4 z0 = *(const f32x4*)&sZ[slot][q8], z1 = *(const f32x4*)&sZ[slot][q8 + 4];
-      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
       if (is_yat(VAR)) {
         n0 = *(const f32x4*)&sNQ[slot][q8];
         n1 = *(const f32x4*)&sNQ[slot][q8 + 4];
       }
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        float wv[2], gv[2], av[2];
+        float v[2], av[2];
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
           const int e = 2 * e2 + o, r = 8 * s + e;
           const float D = e < 4 ? d0[e] : d1[e - 4];
           const float Z = e < 4 ? z0[e] : z1[e - 4];
           const float nq = e < 4 ? n0[e] : n1[e - 4];
-          float bc, lt;
-          pair_terms<VAR>(sacc[r], pacc[r], D, Z, nq + nk, hc, wv[o], gv[o], av[o], bc, lt);
+          if (ROLE_A) {
+            v[o] = pair_weight<VAR>(sacc[r], Z, nq + nk, hc);
+            av[o] = 0.f;
+          } else {
+            float lt;
+            pair_grad<VAR>(sacc[r], pacc[r], D, Z, nq + nk, hc, v[o], av[o], lt);
+          }
           if (MASK) {
             const int qi = qb + q8 + e;
             const bool ok = qi < p.Tq && !(p.causal && my_k > qi);
-            wv[o] = ok ? wv[o] : 0.f;
-            gv[o] = ok ? gv[o] : 0.f;
+            v[o] = ok ? v[o] : 0.f;
             av[o] = ok ? av[o] : 0.f;
           }
         }
-        if (is_a) {
-          pk[s][e2] = pack_bf16(wv[0], wv[1]);
-        } else {
-          pk[s][e2] = pack_bf16(gv[0], gv[1]);
-          if (is_yat(VAR)) corr += (bf16_lo(pk[s][e2]) - av[0]) + (bf16_hi(pk[s][e2]) - av[1]);
-        }
+        pk[s][e2] = pack_bf16(v[0], v[1]);
+        if (!ROLE_A && is_yat(VAR))
+          corr += (bf16_lo(pk[s][e2]) - av[0]) + (bf16_hi(pk[s][e2]) - av[1]);
       }
     }
-    const unsigned short* T = is_a ? sOt[slot] : sQt[slot];
+    const unsigned short* T = ROLE_A ? sOt[slot] : sQt[slot];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const bf16x8 bop = __builtin_bit_cast(bf16x8, pk[s]);
 #pragma unroll
-      for (int i = 0; i < AB; ++i)
-        if (i < (is_a ? VB : KB))
+      for (int i = 0; i < (ROLE_A ? VB : KB); ++i)
           acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&T[(32 * i + col) * TLD + 16 * s + 8 * half]),
                           bop, acc[i]);
     }
@@ -409,8 +436,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
     if (is_a) {
       if (act) {
         const f32x16 none = {};
-        if (need_mask) terms(std::true_type{}, slot, qb, s_cur, none);
-        else terms(std::false_type{}, slot, qb, s_cur, none);
+        if (need_mask) terms(std::true_type{}, std::true_type{}, slot, qb, s_cur, none);
+        else terms(std::false_type{}, std::true_type{}, slot, qb, s_cur, none);
       }
       if (it + 1 < n_it && active(nxt.qt)) scores((it + 1) % NS, (it + 1) & 1, s_cur);
     } else if (act) {
@@ -426,8 +453,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[4 * m + e] = x[e];
       }
-      if (need_mask) terms(std::true_type{}, slot, qb, sacc, pacc);
-      else terms(std::false_type{}, slot, qb, sacc, pacc);
+      if (need_mask) terms(std::true_type{}, std::false_type{}, slot, qb, sacc, pacc);
+      else terms(std::false_type{}, std::false_type{}, slot, qb, sacc, pacc);
     }
     cur = nxt;
     advance(nxt);
@@ -454,12 +481,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
     }
   }
   if (!is_a) {
-    if (is_yat(VAR)) corr = pair_sum(corr);
+    if (is_yat(VAR)) corr = 2.f * pair_sum(corr);  // the kernel carries g/2 and A/2
     if (my_k < p.Tk) {
       unsigned short* dkrow = (unsigned short*)p.dk_ + (int64_t)b * p.ks[0] +
                               (int64_t)hk * p.ks[1] + (int64_t)my_k * p.ks[2];
       const unsigned short* krow = kbase + (int64_t)my_k * p.ks[2];
-      const float sc = is_yat(VAR) ? 1.f : 1.0f / sqrtf((float)DK);
+      const float sc = is_yat(VAR) ? 2.f : 1.0f / sqrtf((float)DK);
 #pragma unroll
       for (int i = 0; i < KB; ++i)
 #pragma unroll
@@ -507,13 +534,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   constexpr int KS = DK / 16, VS = DV / 16;
   constexpr int DKP = DK < 32 ? 32 : DK;
   constexpr int KB = DKP / 32;
-  constexpr int KLD = DK + 8, VLD = DV + 8, TLD = BN + 8;
+  constexpr int KLD = DK + 8, VLD = DV + 8;
   constexpr int K_UNITS = (BN / 4) * (DK / 8), V_UNITS = (BN / 4) * (DV / 8);
   constexpr int UNITS = K_UNITS + V_UNITS;
   constexpr int PER_T = (UNITS + NT - 1) / NT;
 
   __shared__ __attribute__((aligned(16))) unsigned short sK[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sKt[2][DELTA ? 8 : DKP * TLD];
   __shared__ __attribute__((aligned(16))) unsigned short sV[2][BN * VLD];
   __shared__ __attribute__((aligned(16))) float sNK[2][BN];
   __shared__ float sPrm[NW][2];
@@ -607,20 +633,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           *(u32x4*)&sK[buf][k_lds_row(4 * g4 + r) * KLD + 8 * c] = st[i][r];
-        if (!DELTA) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const unsigned a0 = st[i][0][e], a1 = st[i][1][e], a2 = st[i][2][e],
-                           a3 = st[i][3][e];
-            u32x2 lo, hi;
-            lo[0] = (a0 & 0xffffu) | (a1 << 16);
-            lo[1] = (a2 & 0xffffu) | (a3 << 16);
-            hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-            hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            *(u32x2*)&sKt[buf][(8 * c + 2 * e) * TLD + 4 * g4] = lo;
-            *(u32x2*)&sKt[buf][(8 * c + 2 * e + 1) * TLD + 4 * g4] = hi;
-          }
-        }
       } else if (u < UNITS) {
         const int u2 = u - K_UNITS;
         const int g4 = u2 % (BN / 4), c = u2 / (BN / 4);
@@ -635,8 +647,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   f32x16 accQ[KB];
 #pragma unroll
   for (int i = 0; i < KB; ++i) accQ[i] = f32x16{};
-  float corr = 0.f;            // Yat: sum over the lane's keys of B' = bf16(g) - A
-  float sum0 = 0.f, sum1 = 0.f;  // Yat: sum A, sum B; s^tau: sum w (dp - D) log2(phi)
+  float corr = 0.f;            // Yat: sum over the lane's keys of B'/2 = bf16(g/2) - A/2
+  float sum0 = 0.f, sum1 = 0.f;  // Yat: sum A/2, sum B/2; s^tau: sum w (dp - D) log2(phi)
   float dsum = 0.f;            // DELTA: sum over the lane's keys of w dp
 
   // Scores of one tile -> packed gradient scores (pg) and the row sums.
@@ -662,30 +674,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
       }
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        float gv[2], av[2], bv[2], lv[2];
+        float gv[2], av[2], lv[2];
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
           const int e = 2 * e2 + o, r = 8 * s + e;
           const float nkv = e < 4 ? n0[e] : n1[e - 4];
-          float wv;
-          pair_terms<VAR>(sacc[r], pacc[r], D, Z, nq + nkv, hc, wv, gv[o], av[o], bv[o], lv[o]);
-          if (MASK) {
-            const int kj = k0 + k8 + e;
-            const bool ok = my_q < p.Tq && kj < p.Tk && !(p.causal && kj > my_q);
-            wv = ok ? wv : 0.f;
+          const int kj = k0 + k8 + e;
+          const bool ok = !MASK || (my_q < p.Tq && kj < p.Tk && !(p.causal && kj > my_q));
+          if (DELTA) {
+            const float wv = pair_weight<VAR>(sacc[r], Z, nq + nkv, hc);
+            dsum = fmaf(ok ? wv : 0.f, pacc[r], dsum);
+            gv[o] = av[o] = lv[o] = 0.f;
+          } else {
+            pair_grad<VAR>(sacc[r], pacc[r], D, Z, nq + nkv, hc, gv[o], av[o], lv[o]);
             gv[o] = ok ? gv[o] : 0.f;
             av[o] = ok ? av[o] : 0.f;
-            bv[o] = ok ? bv[o] : 0.f;
             lv[o] = ok ? lv[o] : 0.f;
           }
-          if (DELTA) dsum = fmaf(wv, pacc[r], dsum);
         }
         if (DELTA) continue;
         pg[s][e2] = pack_bf16(gv[0], gv[1]);
         if (is_yat(VAR)) {
+          // (g/2 and A/2: the sums are doubled where they are used)
           corr += (bf16_lo(pg[s][e2]) - av[0]) + (bf16_hi(pg[s][e2]) - av[1]);
           sum0 += av[0] + av[1];
-          sum1 += bv[0] + bv[1];
+          sum1 += (gv[0] - av[0]) + (gv[1] - av[1]);
         } else if (VAR == kStau) {
           sum0 += lv[0] + lv[1];
         }
@@ -699,8 +712,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
       const bf16x8 bg = __builtin_bit_cast(bf16x8, pg[s]);
 #pragma unroll
       for (int i = 0; i < KB; ++i)
-        accQ[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sKt[buf][(32 * i + col) * TLD + 16 * s + 8 * half]),
-                         bg, accQ[i]);
+        accQ[i] = mfma32(tr_frag(sK[buf], KLD, 32 * i, s, lane, DK), bg, accQ[i]);
     }
   };
 
@@ -733,12 +745,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
     return;
   }
 
-  if (is_yat(VAR)) corr = pair_sum(corr);
+  if (is_yat(VAR)) corr = 2.f * pair_sum(corr);  // the kernel carries g/2 and A/2
   if (my_q < p.Tq) {
     unsigned short* dqrow = (unsigned short*)p.dq + (int64_t)b * p.qs[0] +
                             (int64_t)h * p.qs[1] + (int64_t)my_q * p.qs[2];
     const unsigned short* qrow = qbase + (int64_t)my_q * p.qs[2];
-    const float sc = is_yat(VAR) ? 1.f : 1.0f / sqrtf((float)DK);
+    const float sc = is_yat(VAR) ? 2.f : 1.0f / sqrtf((float)DK);
 #pragma unroll
     for (int i = 0; i < KB; ++i)
 #pragma unroll

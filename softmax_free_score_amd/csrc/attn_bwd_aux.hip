@@ -55,8 +55,9 @@ __global__ __launch_bounds__(64) void bwd_params(BwdProblem p, int n_qt) {
     s1 += src[2 * t + 1];
   }
   if (is_yat(p.variant)) {
-    if (p.db_raw) p.db_raw[h] = (float)(sigmoid_d(p.b_raw[h]) * s0);
-    if (p.deps_raw) p.deps_raw[h] = (float)(-0.5 * sigmoid_d(p.eps_raw[h]) * s1);
+    // s0 = sum A/2, s1 = sum B/2 (the dq kernel carries halved terms)
+    if (p.db_raw) p.db_raw[h] = (float)(2.0 * sigmoid_d(p.b_raw[h]) * s0);
+    if (p.deps_raw) p.deps_raw[h] = (float)(-sigmoid_d(p.eps_raw[h]) * s1);
   } else if (p.variant == kStau) {
     if (p.dlog_tau) p.dlog_tau[h] = (float)(sigmoid_d(p.log_tau[h]) * 0.6931471805599453 * s0);
   }

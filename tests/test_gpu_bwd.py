@@ -5,7 +5,7 @@ The forward that feeds the backward (its mass and max_score) is the HIP
 forward, as a caller would use it; the oracle takes only the seeded inputs.
 
 Tolerances (bf16 storage, fp32 arithmetic):
-  dq, dk, dv   max |d| <= 3e-2 * S per tensor and mean |d| <= 1e-2 * S_mean,
+  dq, dk, dv   max |d| <= 1.5e-2 * S per tensor and mean |d| <= 5e-3 * S_mean,
                with S = max(max |ref|, 2^-12 max |scale|) and S_mean the same
                with means; "scale" is the oracle's error scale (every factor
                by its absolute value, dw - D by |dw| + |D|).  Normally max
@@ -15,12 +15,14 @@ Tolerances (bf16 storage, fp32 arithmetic):
                fp32 evaluation can only be as close as a few rounding units of
                the terms that cancel.  The products run on bf16 operands: the weights and
                gradient scores are rounded to bf16 (relative 2^-9 each), as are
-               the stored gradients (relative 2^-9 each); the bound allows a
-               few times 2^-9 relative to the largest gradient.
-  parameters   |d| <= 2e-3 * scale per head: the gradient of b_raw, eps_raw
+               the stored gradients.  Measured: max 2.5-6.5e-3 (1.3-3.3 x 2^-9),
+               mean 2.0-3.3e-3; the bounds are 8 x 2^-9 and 2.5 x 2^-9.
+  parameters   |d| <= 1e-6 * scale per head: the gradient of b_raw, eps_raw
                or log_tau is a sum of per-pair terms of both signs, each with
-               the factor dw - D; its rounding (and the D error above) is
-               measured against the same sum of absolute values.
+               the factor dw - D, evaluated in fp32 from fp32 terms (no bf16
+               rounding) and added in fp64 across workgroups; its error is
+               measured against the same sum of absolute values (measured
+               below 1e-7).
 """
 import numpy as np
 import pytest
@@ -33,7 +35,7 @@ from softmax_free_score_amd.workloads import WORKLOADS, make_custom, make_grad_o
 
 pytestmark = pytest.mark.gpu
 
-TOL_MAX, TOL_MEAN, TOL_PARAM = 3e-2, 1e-2, 2e-3
+TOL_MAX, TOL_MEAN, TOL_PARAM = 1.5e-2, 5e-3, 1e-6
 FLOOR = 2.0 ** -12
 PARAMS = {"yat": ("db_raw", "deps_raw"), "stau": ("dlog_tau",), "softmax": ()}
 
