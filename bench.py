@@ -1,7 +1,7 @@
 """Benchmark: fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_yat]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--backward]
 
 A step is one Yat forward (|k|^2 pre-pass + fused kernel, i.e. every step of
 the hot path) over the resident synthetic batch B=4, H=16, T=4096, d=128,
@@ -11,6 +11,11 @@ same inputs for the side-by-side figure.  Prints one JSON line.
 Algorithmic work per allowed (query, key) pair: 2*d_k + 2*d_v MFMA flops
 (elementwise maps and reductions not counted); causal pairs per head
 T(T+1)/2.  Durations are HIP events recorded on the stream the kernels run on.
+
+--backward times attn_bwd instead (the gradients of the same forward, with
+the forward's row statistics and dL/dout resident): five products per pair,
+2*(3 d_k + 2 d_v) flops (S, dP, dV, dK, dQ; the kernels' recomputation of S
+and dP is not counted).  Its line carries its own metric name.
 """
 from __future__ import annotations
 
@@ -72,6 +77,10 @@ def recorded_traffic(workload: str, variant: str):
     if not r or r.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return r.get("bytes_per_launch")
+
+
+def bwd_flops(wl) -> float:
+    return float(wl.allowed_pairs) * 2.0 * (3 * wl.dk + 2 * wl.dv)
 
 
 def time_calls(fn, stream, steps, warmup):
@@ -145,6 +154,8 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=0,
                     help="key chunks per workgroup of the small-grid kernels (0: the library's "
                          "choice, 1: none)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (attn_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -161,6 +172,8 @@ def main():
 
     wl = WORKLOADS[args.workload]
     inp = make_inputs(wl)
+    if args.backward:
+        return bench_backward(args, wl, inp)
     dev = torch.device("cuda:0")
     if wl.dtype == "bf16":
         t = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -253,6 +266,106 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, primary)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_bwd(inp, variant, target_s=10.0):
+    """The fp64 numpy oracle backward over whole (batch, kv head) groups, in
+    order, until about target_s seconds have passed (its own five-product flop
+    count over the pairs it covered)."""
+    import oracle
+    from softmax_free_score_amd.workloads import make_grad_out
+    wl = inp.wl
+    g = wl.Hq // wl.Hkv
+    q, k, v = inp.f64()
+    dout = make_grad_out(inp)[0].astype(np.float64)
+    groups, dt = 0, 0.0
+    while dt < target_s and groups < wl.B * wl.Hkv:
+        b, hk = divmod(groups, wl.Hkv)
+        hs = slice(hk * g, (hk + 1) * g)
+        prm = {n: a[hs].astype(np.float64) for n, a in inp.params().items()}
+        t0 = time.perf_counter()
+        oracle.attn_bwd_np(q[b:b + 1, hs], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1],
+                           dout[b:b + 1, hs], variant, causal=wl.causal, **prm)
+        dt += time.perf_counter() - t0
+        groups += 1
+    pairs = groups * g * (wl.Tq * (wl.Tq + 1) // 2 if wl.causal else wl.Tq * wl.Tk)
+    flops = pairs * 2.0 * (3 * wl.dk + 2 * wl.dv)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except ImportError:
+        cores = os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{variant}, {groups} of {wl.B * wl.Hkv} (batch, kv head) groups "
+                      f"({groups * g} query heads, {pairs} pairs) of {wl.name} in {dt:.1f} s, "
+                      f"fp64 numpy (BLAS threads for the products)"}
+
+
+def bench_backward(args, wl, inp):
+    import torch
+    from softmax_free_score_amd import attn
+    from softmax_free_score_amd.workloads import make_grad_out
+
+    dev = torch.device("cuda:0")
+    t = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    if wl.dtype != "bf16":
+        print("the backward is built for bf16 storage", file=sys.stderr)
+        sys.exit(2)
+    q, k, v = t(inp.q_bits), t(inp.k_bits), t(inp.v_bits)
+    dout = t(make_grad_out(inp)[1])
+    prm = {n: torch.from_numpy(a).to(dev) for n, a in inp.params().items()}
+    stream = torch.cuda.current_stream(dev)
+    grads = {n: torch.empty_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v))}
+
+    def call(var):
+        _, mass, mx = attn.attn_fwd(q, k, v, var, causal=wl.causal, **prm)
+        n = attn.bwd_workspace_bytes(q, k, v, var)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+
+        def run():
+            attn.attn_bwd(q, k, v, dout, var, mass, mx, causal=wl.causal, workspace=ws,
+                          stream=stream.cuda_stream, **grads, **prm)
+        return run
+
+    flops = bwd_flops(wl)
+    primary = args.variant
+    torch.cuda.synchronize()
+    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup)
+    others = {}
+    for var in wl.variants:
+        if var != primary:
+            m2, _, _ = time_calls(call(var), stream, args.steps, args.warmup)
+            others[var] = {"ms": m2, "tflops": flops / (m2 * 1e-3) / 1e12,
+                           "frac_bf16_peak": flops / (m2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    value = flops / (mean_ms * 1e-3) / 1e12
+    line = {
+        "metric": "attn bwd TFLOP/s (5-product count) and % bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} Tq{wl.Tq} Tk{wl.Tk} "
+                               f"dk{wl.dk} dv{wl.dv} {wl.dtype} "
+                               f"{'causal' if wl.causal else 'non-causal'}, backward",
+                   "variant": primary, "global_batch": wl.B, "seq_len": wl.Tq,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": f"attn_bwd ({primary}): row prep, D pass, dK/dV and dQ kernels; "
+                               f"flops = {flops:.4e} per call ({wl.allowed_pairs} allowed "
+                               f"pairs x 2(3 dk + 2 dv))",
+                     "median_ms": round(med_ms, 4)},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    for var, r in others.items():
+        line[var] = {k2: round(v2, 4) for k2, v2 in r.items()}
+    if "softmax" in others:
+        line[f"{primary}_speed_vs_softmax"] = round(others["softmax"]["ms"] / mean_ms, 4)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(inp, primary)
     print(json.dumps(line), flush=True)
 
 
