@@ -73,6 +73,35 @@ namespace {
 __device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
+// A-operand fragment of v_mfma_f32_32x32x16_bf16 whose matrix is the
+// transpose of a row-major LDS tile R (32 rows, pitch `ld` elements, row j
+// stored at position k_lds_row(j)): lane (half, col) receives column
+// c0 + col of tile rows 16 s + 8 half .. 16 s + 8 half + 7.  Two
+// ds_read_b64_tr_b16 per lane: within each group of 16 lanes, source lane c
+// addresses tile row base + c / 4, columns cb + 4 (c % 4) .. + 3, and the
+// hardware returns to lane i of the group column cb + i of rows base .. base
+// + 3 (lane mapping measured on gfx950).  Columns at or past `width` (a tile
+// narrower than 32) wrap to width - 16 .. width - 1; those rows of the
+// product are not used.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned short* R, int ld, int c0, int s,
+                                          int lane, int width) {
+  const int g = lane >> 4, c = lane & 15;
+  int cb = c0 + 16 * (g & 1) + 4 * (c & 3);
+  if (cb >= width) cb -= 16;
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * s + 8 * (g >> 1) + 4 * j + (c >> 2);
+    const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(R + k_lds_row(row) * ld + cb));
+    const u32x2 xx = __builtin_bit_cast(u32x2, x);
+    out[2 * j] = xx[0];
+    out[2 * j + 1] = xx[1];
+  }
+  return __builtin_bit_cast(bf16x8, out);
+}
+
 // Per-head constants of a map.
 struct HeadC {
   float bias, eps, tau, scale, c_sm;
