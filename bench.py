@@ -148,7 +148,7 @@ def main():
                     help="cycle over enough distinct copies of the inputs and outputs to "
                          "span this many MiB (larger than the 256 MB Infinity Cache, so "
                          "small workloads are measured from HBM)")
-    ap.add_argument("--block-rows", type=int, default=0, choices=(0, 64, 128, 256),
+    ap.add_argument("--block-rows", type=int, default=0, choices=(0, 8, 64, 128, 256),
                     help="query rows per workgroup of the bf16 kernel (0: the library's "
                          "choice from the grid size)")
     ap.add_argument("--kv-splits", type=int, default=0,

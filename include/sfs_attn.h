@@ -85,10 +85,14 @@ typedef struct {
   int64_t B, Hq, Hkv, Tq, Tk, dk, dv;
   int32_t dtype; /* attn_dtype */
   /* Query rows per workgroup of the bf16 path: 0 lets the library choose
-   * from the grid size (256-row workgroups when there are enough to fill
-   * the device, else 128 or 64); 64, 128 or 256 force that kernel.  Every
-   * choice computes the same map; results may differ in the last bits only
-   * through the order of the softmax rescale.  The fp32 path takes 0 only. */
+   * (8 when a key/value head has at most 8 query rows, Hq/Hkv * Tq <= 8;
+   * else 256-row workgroups when there are enough to fill the device, else
+   * 128 or 64); 8, 64, 128 or 256 force that kernel.  8 is the decode
+   * kernel: the query rows of a key/value head packed into one workgroup per
+   * 256 keys on the vector ALU, each key and value row read once, partials
+   * merged as with kv_splits (it needs Hq/Hkv * Tq <= 8).  Every choice
+   * computes the same map; results may differ in the last bits through the
+   * order of fp32 additions.  The fp32 path takes 0 only. */
   int32_t block_rows;
   int64_t q_stride[3];
   int64_t k_stride[3];
@@ -102,7 +106,8 @@ typedef struct {
    * second kernel merges them: plain sums for Yat and s^tau, whose weights
    * need no running maximum, and the log-sum-exp merge for softmax.
    * 0 lets the library choose; 1 switches splitting off; 2 .. 64 force that
-   * many chunks (bf16 only, not with block_rows = 256).  Results differ from
+   * many chunks (bf16 only, not with block_rows = 256 or 8; the decode
+   * kernel always splits into 256-key chunks).  Results differ from
    * the unsplit ones only in the order of fp32 additions. */
   int32_t kv_splits;
   int32_t reserved; /* must be 0 */

@@ -44,11 +44,12 @@ struct WsLayout {
 };
 WsLayout ws_layout(const attn_desc* d, int variant, int causal) {
   WsLayout w{};
-  w.plan = sfs::make_plan(d->B, d->Hq, d->Tq, d->Tk, causal, d->block_rows, d->kv_splits);
+  w.plan = sfs::make_plan(d->B, d->Hq, d->Hkv, d->Tq, d->Tk, causal, d->block_rows,
+                          d->kv_splits);
   w.nk_bytes = variant == ATTN_YAT ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
   w.part_off = (w.nk_bytes + 255) / 256 * 256;
   w.total = w.nk_bytes;
-  if (w.plan.splits > 1)
+  if (w.plan.splits > 1 || w.plan.rows == sfs::kDecodeRows)
     w.total = w.part_off + (size_t)w.plan.splits * (size_t)(d->B * d->Hq * d->Tq) *
                                (size_t)(d->dv + 4) * sizeof(float);
   return w;
@@ -97,12 +98,18 @@ int validate(const attn_desc* d, const void* q, const void* k, const void* v, in
     return ATTN_ERR_UNSUPPORTED;
   }
   if (d->block_rows != 0 && (d->dtype != ATTN_BF16 || (d->block_rows != 64 &&
-                             d->block_rows != 128 && d->block_rows != 256))) {
-    set_error("block_rows must be 0, or 64, 128 or 256 with bf16 storage");
+                             d->block_rows != 128 && d->block_rows != 256 &&
+                             d->block_rows != sfs::kDecodeRows))) {
+    set_error("block_rows must be 0, or 8, 64, 128 or 256 with bf16 storage");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (d->block_rows == sfs::kDecodeRows && d->Hq / d->Hkv * d->Tq > sfs::kDecodeRows) {
+    set_error("block_rows = 8 needs at most 8 query rows per key/value head (Hq/Hkv * Tq)");
     return ATTN_ERR_UNSUPPORTED;
   }
   if (d->kv_splits < 0 || d->kv_splits > sfs::kMaxKvSplits || d->reserved != 0 ||
-      (d->kv_splits > 1 && (d->dtype != ATTN_BF16 || d->block_rows == 256))) {
+      (d->kv_splits > 1 && (d->dtype != ATTN_BF16 || d->block_rows == 256 ||
+                            d->block_rows == sfs::kDecodeRows))) {
     set_error("kv_splits must be 0 .. 64; more than 1 needs bf16 and a 64- or 128-row kernel");
     return ATTN_ERR_UNSUPPORTED;
   }
@@ -202,7 +209,8 @@ int run(const attn_desc* d, const void* q, const void* k, const void* v, int var
     const WsLayout w = ws_layout(d, variant, p.causal);
     p.block_rows = w.plan.rows;
     p.kv_splits = w.plan.splits;
-    if (p.kv_splits > 1) p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part_off);
+    if (p.kv_splits > 1 || p.block_rows == sfs::kDecodeRows)
+      p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part_off);
   }
   p.yat_power = yat_power;
   p.yat_bias_free = yat_bias_free ? 1 : 0;
@@ -214,13 +222,23 @@ int run(const attn_desc* d, const void* q, const void* k, const void* v, int var
     if (d->dtype == ATTN_F32) {
       e = sfs::launch_f32(p, s);
     } else {
-      switch (p.dk) {
-        case 16: e = sfs::launch_bf16_dk16(p, s); break;
-        case 32: e = sfs::launch_bf16_dk32(p, s); break;
-        case 64: e = sfs::launch_bf16_dk64(p, s); break;
-        default: e = sfs::launch_bf16_dk128(p, s); break;
+      if (p.block_rows == sfs::kDecodeRows) {
+        switch (p.dk) {
+          case 16: e = sfs::launch_decode_bf16_dk16(p, s); break;
+          case 32: e = sfs::launch_decode_bf16_dk32(p, s); break;
+          case 64: e = sfs::launch_decode_bf16_dk64(p, s); break;
+          default: e = sfs::launch_decode_bf16_dk128(p, s); break;
+        }
+      } else {
+        switch (p.dk) {
+          case 16: e = sfs::launch_bf16_dk16(p, s); break;
+          case 32: e = sfs::launch_bf16_dk32(p, s); break;
+          case 64: e = sfs::launch_bf16_dk64(p, s); break;
+          default: e = sfs::launch_bf16_dk128(p, s); break;
+        }
       }
-      if (e == hipSuccess && p.kv_splits > 1) e = sfs::launch_combine(p, s);
+      if (e == hipSuccess && (p.kv_splits > 1 || p.block_rows == sfs::kDecodeRows))
+        e = sfs::launch_combine(p, s);
     }
   }
   if (e != hipSuccess) {

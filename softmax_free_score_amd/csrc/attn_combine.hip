@@ -1,4 +1,4 @@
-// attn_combine.hip -- merges the key-chunk partials of the small-grid kernels.
+// attn_combine.hip -- merges the key-chunk partials of the small-grid and decode kernels.
 //
 // When the keys of a workgroup are split into S chunks, chunk s of query row
 // r leaves O_s (sum over its keys of w_j v_j, unnormalised), its mass m_s, its
@@ -14,8 +14,11 @@
 //               O = sum 2^(M_s - M) O_s, l = sum 2^(M_s - M) m_s, out = O / l,
 //               mass reported relative to the row maximum x = max x_s.
 //
-// One wave per row; lane c holds value columns c and c + 64.  The merge runs
-// over s in order, so the result does not depend on scheduling.
+// One wave per row.  The chunk statistics are read 64 at a time, one chunk
+// per lane, and reduced across the wave; the value columns (lane c holds c
+// and c + 64) then accumulate the chunks' partial O eight loads at a time, in
+// chunk order.  Every reduction has a fixed order, so the result does not
+// depend on scheduling.
 #include "attn_launch.h"
 
 namespace sfs {
@@ -26,31 +29,68 @@ constexpr float kLn2c = 0.6931471805599453f;
 __device__ __forceinline__ unsigned short to_bf16(float x) {
   return __builtin_bit_cast(unsigned short, (__bf16)x);  // round to nearest even
 }
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
 
 __global__ __launch_bounds__(256) void combine_partials(Problem p) {
   const int lane = threadIdx.x & 63;
   const int64_t R = (int64_t)p.B * p.Hq * p.Tq;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
+  if (r >= R) return;  // whole waves
   const int S = p.kv_splits, dv = p.dv;
   const float* po = p.part;
   const float* ps = p.part + (int64_t)S * R * dv;
 
-  float M = -INFINITY, x = -INFINITY;
-  for (int s = 0; s < S; ++s) {
-    const float* st = ps + ((int64_t)s * R + r) * 4;
-    x = fmaxf(x, st[1]);
-    M = fmaxf(M, st[2]);
+  float x = -INFINITY, M = -INFINITY;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < S) {
+      const float* st = ps + ((int64_t)s * R + r) * 4;
+      x = fmaxf(x, st[1]);
+      M = fmaxf(M, st[2]);
+    }
   }
+  x = wave_max(x);
+  M = wave_max(M);
   float mass = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* st = ps + ((int64_t)s * R + r) * 4;
-    float wgt = 1.f;
-    if (p.variant == kSoftmax) wgt = st[2] == -INFINITY ? 0.f : exp2f(st[2] - M);
-    mass += wgt * st[0];
-    const float* row = po + ((int64_t)s * R + r) * dv;
-    if (lane < dv) o0 += wgt * row[lane];
-    if (lane + 64 < dv) o1 += wgt * row[lane + 64];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    // lane l: the weight and weighted mass of chunk s0 + l
+    float wgt = 0.f, m = 0.f;
+    const int s = s0 + lane;
+    if (s < S) {
+      const float* st = ps + ((int64_t)s * R + r) * 4;
+      wgt = 1.f;
+      if (p.variant == kSoftmax) wgt = st[2] == -INFINITY ? 0.f : exp2f(st[2] - M);
+      m = wgt * st[0];
+    }
+    mass += wave_sum(m);
+    const int nb = min(64, S - s0);
+    for (int t = 0; t < nb; t += 8) {
+      float a0[8], a1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a0[u] = a1[u] = 0.f;
+        if (t + u < nb) {
+          const float* row = po + ((int64_t)(s0 + t + u) * R + r) * dv;
+          if (lane < dv) a0[u] = row[lane];
+          if (lane + 64 < dv) a1[u] = row[lane + 64];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __shfl(wgt, t + u, 64);  // 0 past the last chunk
+        o0 = fmaf(wu, a0[u], o0);
+        o1 = fmaf(wu, a1[u], o1);
+      }
+    }
   }
   float inv;
   if (is_yat(p.variant)) inv = 1.f / (mass + 1e-9f);

@@ -37,12 +37,21 @@ __host__ __device__ inline int64_t nk_pitch(int64_t Tk) { return (Tk + 63) / 64 
 // each chunk writes unnormalised partials that a combine kernel merges.
 constexpr int kDeviceCUs = 256;
 constexpr int kMaxKvSplits = 64;
+// rows = kDecodeRows: the vector kernel for at most this many query rows per
+// key/value head (the g heads of a group x T_q packed together), one
+// workgroup per kDecodeChunk keys, always writing partials.
+constexpr int kDecodeRows = 8;
+constexpr int kDecodeChunk = 256;
 struct Plan {
   int rows;
   int splits;
 };
-inline Plan make_plan(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int causal, int block_rows,
-                      int kv_splits) {
+inline Plan make_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int causal,
+                      int block_rows, int kv_splits) {
+  const int64_t packed = (Hq / Hkv) * Tq;
+  if (block_rows == kDecodeRows ||
+      (block_rows == 0 && kv_splits == 0 && packed <= kDecodeRows))
+    return Plan{kDecodeRows, (int)((Tk + kDecodeChunk - 1) / kDecodeChunk)};
   const int64_t bh = B * Hq;
   const int64_t n256 = (Tq + 255) / 256 * bh, n128 = (Tq + 127) / 128 * bh,
                 n64 = (Tq + 63) / 64 * bh;
@@ -88,7 +97,8 @@ struct Problem {
   int B, Hq, Hkv, Tq, Tk, dk, dv;
   int variant;
   int causal;
-  int block_rows;     // query rows per workgroup: 64, 128 or 256 (bf16; planned)
+  int block_rows;     // query rows per workgroup: 64, 128 or 256, or kDecodeRows for
+                      // the packed vector kernel (bf16; planned)
   int kv_splits;      // key chunks per workgroup (>= 1); > 1 writes partials
   float* part;        // kv_splits > 1: partial O [S][R][dv] then stats [S][R][4]
                       // (mass, max, reference max), R = B*Hq*Tq
@@ -117,6 +127,13 @@ constexpr int kStatsRows = 64;
 
 // Merges the kv_splits partials of every row into out, mass and max_score.
 hipError_t launch_combine(const Problem& p, hipStream_t stream);
+
+// Forward for at most kDecodeRows query rows per key/value head (vector ALU,
+// partials per kDecodeChunk keys; combine_partials merges them).
+hipError_t launch_decode_bf16_dk16(const Problem& p, hipStream_t stream);
+hipError_t launch_decode_bf16_dk32(const Problem& p, hipStream_t stream);
+hipError_t launch_decode_bf16_dk64(const Problem& p, hipStream_t stream);
+hipError_t launch_decode_bf16_dk128(const Problem& p, hipStream_t stream);
 
 // Fused forward for fp32 storage (vector-ALU path).
 hipError_t launch_f32(const Problem& p, hipStream_t stream);

@@ -280,3 +280,28 @@ def test_bwd_workspace_bytes():
     assert ws(7) == 0
     d.dtype = attn.ATTN_F32
     assert ws(attn.ATTN_SOFTMAX) == 0
+
+
+@pytest.mark.parametrize("shape,rows,splits,dtype,status", [
+    ((1, 2, 1, 4, 64), 8, 0, attn.ATTN_BF16, ERR_HIP),    # 2 x 4 = 8 packed rows: valid
+    ((1, 2, 1, 5, 64), 8, 0, attn.ATTN_BF16, ERR_UNSUP),  # 10 rows per kv head
+    ((1, 8, 1, 1, 64), 8, 0, attn.ATTN_BF16, ERR_HIP),
+    ((1, 8, 1, 1, 64), 8, 2, attn.ATTN_BF16, ERR_UNSUP),  # the decode kernel chunks by itself
+    ((1, 8, 1, 1, 64), 8, 0, attn.ATTN_F32, ERR_UNSUP)])
+def test_decode_kernel_validation(shape, rows, splits, dtype, status):
+    B, Hq, Hkv, Tq, Tk = shape
+    d = desc(B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, dtype=dtype)
+    d.block_rows, d.kv_splits = rows, splits
+    assert call(d, causal=0, ws_bytes=1 << 30) == status
+
+
+def test_decode_kernel_workspace():
+    # 4 query rows per kv head: the decode kernel, 256-key chunks, partials for
+    # every chunk (2 x 8 x 1 = 16 rows x (128 + 4) floats), also when one chunk
+    d = desc(B=2, Hq=8, Hkv=2, Tq=1, Tk=4096, dk=128, dv=128)
+    assert ws(d, attn.ATTN_SOFTMAX) == 16 * 16 * 132 * 4
+    d = desc(B=2, Hq=8, Hkv=2, Tq=1, Tk=100, dk=128, dv=128)
+    assert ws(d, attn.ATTN_SOFTMAX) == 1 * 16 * 132 * 4
+    d.block_rows = 64                                    # forced tile kernel: no partials
+    assert ws(d, attn.ATTN_SOFTMAX) == 0
+

@@ -182,6 +182,36 @@ def test_decode_shapes(variant, shape):
     full_check(inp, variant, False, "decode")
 
 
+DECODE_FORCED = [
+    # B, Hq, Hkv, Tq, Tk, dk, dv, causal; Hq/Hkv * Tq <= 8
+    (2, 4, 2, 1, 1000, 64, 128, False),
+    (1, 8, 1, 1, 300, 128, 16, False),      # g = 8, d_v = 16
+    (3, 6, 3, 2, 257, 128, 128, False),     # 4 packed rows, one key past a chunk
+    (1, 4, 4, 2, 700, 16, 64, False),       # d_k = 16
+    (1, 2, 2, 3, 3, 32, 32, True),          # causal, fewer keys than a chunk
+    (2, 2, 1, 4, 4, 128, 128, True),        # causal, 8 packed rows
+]
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", DECODE_FORCED, ids=lambda s: "x".join(map(str, s)))
+def test_decode_kernel(variant, shape):
+    # the packed vector kernel (block_rows = 8) and the library's own choice
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=23, qk_std=1.5)
+    full_check(inp, variant, causal, "decode_kernel", block_rows=(8, 0))
+
+
+def test_decode_kernel_tied_and_yat_options():
+    # k := q puts the peak (|q|^2 + b)^2 / eps on the diagonal; the kernel's
+    # |q|^2, |k|^2 and q.k share one FMA order, so d2 is exactly 0 there
+    inp = make_custom(1, 4, 4, 2, 2, 128, 128, "bf16", True, seed=24, qk_std=2.0, tied=True)
+    full_check(inp, "yat", True, "decode_tied", block_rows=(8,))
+    inp = make_custom(2, 8, 2, 1, 900, 128, 128, "bf16", False, seed=25, qk_std=1.0)
+    for opts in ((2, False), (3, True), (1, True)):
+        full_check(inp, "yat", False, "decode_yat_opts", block_rows=(8,), yat_opts=opts)
+
+
 def test_kv_splits_more_chunks_than_tiles():
     # 64 chunks over 4 tiles of keys: most chunks are empty and write neutral partials
     inp = make_custom(1, 2, 2, 40, 100, 64, 64, "bf16", False, seed=21)
