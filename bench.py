@@ -40,6 +40,18 @@ def alg_flops(wl) -> float:
     return float(wl.allowed_pairs) * 2.0 * (wl.dk + wl.dv)
 
 
+def kernels_timed(wl, args, variant) -> str:
+    """The kernels one timed forward call runs, by the library's plan: the
+    decode kernel and its merge when a key/value head has at most 8 query
+    rows (or block_rows = 8 forces it), else the fused tile kernel, after the
+    |k|^2 pre-pass for Yat."""
+    packed = wl.Hq // wl.Hkv * wl.Tq
+    if args.block_rows == 8 or (args.block_rows == 0 and args.kv_splits == 0 and packed <= 8):
+        return f"attn_decode_bf16 ({variant}) + combine_partials"
+    pre = "|k|^2 pre-pass + " if variant == "yat" else ""
+    return f"{pre}attn_fwd_bf16 ({variant})"
+
+
 def alg_bytes(wl) -> float:
     e = 2 if wl.dtype == "bf16" else 4
     q = wl.B * wl.Hq * wl.Tq * wl.dk * e
@@ -240,7 +252,7 @@ def main():
         "roofline": {**roof,
                      "traffic": recorded_traffic(wl.name, primary),
                      "traffic_unit": "bytes per launch of attn_fwd_bf16 (HBM, counters)",
-                     "kernel": f"|k|^2 pre-pass + attn_fwd_bf16 ({primary}); flops = "
+                     "kernel": f"{kernels_timed(wl, args, primary)}; flops = "
                                f"{flops:.4e} per launch ({wl.allowed_pairs} allowed pairs x "
                                f"2(dk+dv))",
                      "median_ms": round(med_ms, 4),

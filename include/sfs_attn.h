@@ -119,9 +119,11 @@ int attn_desc_init(attn_desc* desc, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
                    int64_t Tk, int64_t dk, int64_t dv, int32_t dtype);
 
 /* Device workspace, in bytes, that attn_fwd needs for this problem and map:
- * fp32 |k|^2 per key row for ATTN_YAT with bf16 storage, and, when the keys
- * are split (see kv_splits), fp32 partials of 4 (d_v + 4) bytes per query row
- * and chunk.  Returns 0 when none is needed or the description is invalid. */
+ * fp32 |k|^2 per key row for ATTN_YAT with bf16 storage (not for the decode
+ * kernel, block_rows = 8, which forms it itself), and, when the keys are split
+ * (see kv_splits; the decode kernel always is, in 256-key chunks), fp32
+ * partials of 4 (d_v + 4) bytes per query row and chunk.  Returns 0 when none
+ * is needed or the description is invalid. */
 size_t attn_fwd_workspace_bytes(const attn_desc* desc, int variant);
 
 /* Attention forward.

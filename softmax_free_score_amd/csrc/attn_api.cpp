@@ -46,10 +46,13 @@ WsLayout ws_layout(const attn_desc* d, int variant, int causal) {
   WsLayout w{};
   w.plan = sfs::make_plan(d->B, d->Hq, d->Hkv, d->Tq, d->Tk, causal, d->block_rows,
                           d->kv_splits);
-  w.nk_bytes = variant == ATTN_YAT ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
+  // the decode kernel forms |k|^2 itself: no pre-pass
+  const bool decode = w.plan.rows == sfs::kDecodeRows;
+  w.nk_bytes = variant == ATTN_YAT && !decode
+                   ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
   w.part_off = (w.nk_bytes + 255) / 256 * 256;
   w.total = w.nk_bytes;
-  if (w.plan.splits > 1 || w.plan.rows == sfs::kDecodeRows)
+  if (w.plan.splits > 1 || decode)
     w.total = w.part_off + (size_t)w.plan.splits * (size_t)(d->B * d->Hq * d->Tq) *
                                (size_t)(d->dv + 4) * sizeof(float);
   return w;

@@ -300,6 +300,7 @@ def test_decode_kernel_workspace():
     # every chunk (2 x 8 x 1 = 16 rows x (128 + 4) floats), also when one chunk
     d = desc(B=2, Hq=8, Hkv=2, Tq=1, Tk=4096, dk=128, dv=128)
     assert ws(d, attn.ATTN_SOFTMAX) == 16 * 16 * 132 * 4
+    assert ws(d, attn.ATTN_YAT) == 16 * 16 * 132 * 4     # no |k|^2 pre-pass buffer
     d = desc(B=2, Hq=8, Hkv=2, Tq=1, Tk=100, dk=128, dv=128)
     assert ws(d, attn.ATTN_SOFTMAX) == 1 * 16 * 132 * 4
     d.block_rows = 64                                    # forced tile kernel: no partials

@@ -190,6 +190,8 @@ DECODE_FORCED = [
     (1, 4, 4, 2, 700, 16, 64, False),       # d_k = 16
     (1, 2, 2, 3, 3, 32, 32, True),          # causal, fewer keys than a chunk
     (2, 2, 1, 4, 4, 128, 128, True),        # causal, 8 packed rows
+    (1, 2, 1, 1, 17000, 64, 64, False),     # 67 chunks: the merge reads more than 64
+    (2, 3, 3, 1, 513, 32, 32, False),       # one row per kv head, ragged last chunk
 ]
 
 
