@@ -119,7 +119,8 @@ int attn_desc_init(attn_desc* desc, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
                    int64_t Tk, int64_t dk, int64_t dv, int32_t dtype);
 
 /* Device workspace, in bytes, that attn_fwd needs for this problem and map:
- * fp32 |k|^2 per key row for ATTN_YAT with bf16 storage (not for the decode
+ * fp32 |k|^2 + b per key row and query head for ATTN_YAT with bf16 storage
+ * (B * Hq * T_k rounded up to 64 rows; not for the decode
  * kernel, block_rows = 8, which forms it itself), and, when the keys are split
  * (see kv_splits; the decode kernel always is, in 256-key chunks), fp32
  * partials of 4 (d_v + 4) bytes per query row and chunk.  Returns 0 when none
@@ -235,7 +236,10 @@ int attn_telemetry(const attn_desc* desc, const void* q, const void* k, int vari
  * q, k, v        the forward's inputs, device bf16, strides of desc.
  * dout           device bf16 [B,Hq,Tq,dv], strides desc->o_stride.
  * mass,          the forward's row statistics, device fp32 [B,Hq,Tq],
- * max_score      contiguous; mass always, max_score for ATTN_SOFTMAX.
+ * max_score      contiguous: mass for ATTN_SOFTMAX and ATTN_STAU, max_score
+ *                for ATTN_SOFTMAX.  ATTN_YAT reads neither (may be NULL): it
+ *                forms mass + 1e-9 again from the kappa it differentiates,
+ *                so that the weights and their normaliser round alike.
  * dq, dk, dv     device bf16 outputs laid out like q, k and v (q_stride,
  *                k_stride, v_stride); every element is written (dk = dv = 0
  *                when T_q == 0).  They must not alias any input.

@@ -49,7 +49,7 @@ WsLayout ws_layout(const attn_desc* d, int variant, int causal) {
   // the decode kernel forms |k|^2 itself: no pre-pass
   const bool decode = w.plan.rows == sfs::kDecodeRows;
   w.nk_bytes = variant == ATTN_YAT && !decode
-                   ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
+                   ? (size_t)(d->B * d->Hq * sfs::nk_pitch(d->Tk)) * 4 : 0;
   w.part_off = (w.nk_bytes + 255) / 256 * 256;
   w.total = w.nk_bytes;
   if (w.plan.splits > 1 || decode)
@@ -413,9 +413,10 @@ int attn_bwd(const attn_desc* d, const void* q, const void* k, const void* v,
                     workspace, workspace_bytes, false, &empty, need);
   if (st != ATTN_OK) return st;
   if (!empty) {
-    if (!dq || !dk || !dv || !mass || (variant == ATTN_SOFTMAX && !max_score)) {
-      set_error("the backward needs dq, dk, dv, the forward's mass and, for softmax, "
-                "its max_score");
+    if (!dq || !dk || !dv || (variant != ATTN_YAT && !mass) ||
+        (variant == ATTN_SOFTMAX && !max_score)) {
+      set_error("the backward needs dq, dk, dv, the forward's mass (softmax, s^tau) and, "
+                "for softmax, its max_score");
       return ATTN_ERR_NULL;
     }
     if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) {

@@ -1,8 +1,8 @@
 // attn_bf16.hip -- fused attention forward for bf16 storage on gfx950.
 //
 // Compiled once per key width: -DSFS_DK=16|32|64|128.  Each translation unit
-// holds the |k|^2 pre-pass for that width and the fused kernel for the three
-// score-to-weight maps x four value widths.
+// holds the Yat |k|^2 pre-pass for that width and the fused kernels for the
+// three score-to-weight maps x four value widths.
 //
 // What is computed (per batch b, query head h, query row i; h_kv = h / g):
 //   Yat     ("Softmax-Free Attention in JAX/Flax NNX", "One module, two
@@ -32,12 +32,13 @@
 //   * The two halves of the workgroup run a "ping-pong" schedule (see the
 //     kernel): on each SIMD one wave issues the matrix-core work of a tile
 //     while its partner maps the previous scores to weights on the vector ALU.
-//   * The Yat distance is built in registers from the same score tile:
-//     d2 = (|q|^2 + |k|^2) - 2 s.  |k|^2 comes from a pre-pass and |q|^2 from
-//     the workgroup's own query fragments; both use the same MFMA instruction
-//     and k-step order as the score tile (diagonals of X X^T), so for a key
-//     equal to its query the three terms cancel to exactly 0 and the peak
-//     (|q|^2 + b)^2 / eps is reproduced.
+//   * The Yat distance is built in registers from the same score tile.  The
+//     score chain starts at b, so it yields u = q.k + b, and d2 = (|q|^2 + b)
+//     + (|k|^2 + b) - 2u.  |k|^2 + b comes from a pre-pass (per query head)
+//     and |q|^2 + b from the workgroup's own query fragments; both use the
+//     same MFMA instruction, k-step order and start value as the score tile
+//     (diagonals of X X^T), so for a key equal to its query the three terms
+//     cancel to exactly 0 and the peak (|q|^2 + b)^2 / eps is reproduced.
 //   * Yat and s^tau accumulate sum(p v) and the mass in one pass with no
 //     running maximum; softmax keeps a reference maximum that moves only when
 //     a tile's maximum exceeds it by more than 2^8 (then O and the sum are
@@ -65,6 +66,51 @@ namespace {
 // moved when a tile's maximum exceeds it by more than this (log2 units):
 // weights stay below 2^8 and most tiles skip the rescale of the accumulator.
 constexpr float kRescaleSlack = 8.0f;
+
+// Start value of the score accumulators.  Yat starts every MFMA chain -- the
+// score q.k and the diagonals |q|^2 and |k|^2 -- at b: the chain then hands
+// over u = q.k + b, the numerator's base, and the distance is
+// d2 = (|q|^2 + b) + (|k|^2 + b) - 2u, with no add of b per element.  For a
+// key equal to its query the three chains are the same instruction sequence
+// from the same start, so d2 is still exactly 0.  The other maps start at 0.
+template <int VAR>
+__device__ __forceinline__ f32x16 score_init(float bias) {
+  f32x16 c = {};
+  if constexpr (is_yat(VAR)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = bias;
+  }
+  return c;
+}
+
+// Yat's b of query head h (0 for the bias-free form).
+__device__ __forceinline__ float yat_bias(const Problem& p, int h) {
+  return p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
+}
+
+// Yat pre-pass: |k_j|^2 + b_h for every key row and query head, by the same
+// MFMA sequence and start value as the score tile (see score_init).  One wave
+// per 32 rows; grid (ceil(T_k / 128), Hq, B), 256 threads; output
+// [B][Hq][nk_pitch(T_k)].
+template <int DK>
+__global__ __launch_bounds__(256) void yat_key_norms_bf16(Problem p) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y, hk = h / (p.Hq / p.Hkv);
+  const int row = blockIdx.x * 128 + 32 * w + col;
+  const unsigned short* base =
+      (const unsigned short*)p.k + (int64_t)b * p.ks[0] + (int64_t)hk * p.ks[1];
+  const uint32_t bytes = slice_bytes(p.Tk, p.ks[2], DK);
+  const rsrc_t r = make_rsrc(base, bytes);
+  const uint32_t off = row < p.Tk ? (uint32_t)(((int64_t)row * p.ks[2] + 8 * half) * 2) : bytes;
+  f32x16 g = score_init<kYat>(yat_bias(p, h));
+#pragma unroll
+  for (int s = 0; s < DK / 16; ++s)
+    g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
+               __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
+  if (row < p.Tk && holds_diag(col, half))
+    p.nk[((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) + row] = diag_of(g, col);
+}
 
 // Fused forward, "ping-pong" schedule.
 //
@@ -140,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   // Per-head scalars (prologue).
   float bias = 0.f, eps = 0.f, tau = 0.f;
   if (is_yat(VAR)) {
-    bias = p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
+    bias = yat_bias(p, h);
     eps = softplus_precise(p.eps_raw[h]);
   } else if (VAR == kStau) {
     tau = softplus_precise(p.log_tau[h]) + 1.f;
@@ -160,12 +206,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
     __builtin_amdgcn_s_waitcnt(0);
   }
   float nq = 0.f;
-  // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
+  // |k|^2 + b slice of this query head; padded to a multiple of 64 rows, so a
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
-      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;
+  const f32x16 sinit = score_init<VAR>(bias);
   if (is_yat(VAR)) {
-    f32x16 g = {};
+    f32x16 g = sinit;
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
     if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
@@ -174,9 +221,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
 
-  // Staging registers: group 0 stages K (+ |k|^2), group 1 stages V.
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[V_PER_T][4];
+  // Staging registers: group 0 stages K (+ |k|^2), group 1 stages V; one
+  // array serves both, since a wave only ever stages one of them.
+  constexpr int NSTG = K_PER_T > 4 * V_PER_T ? K_PER_T : 4 * V_PER_T;
+  u32x4 stg[NSTG];
   f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
 
   auto load_k = [&](int k0) {
@@ -186,7 +234,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
       if (u < K_UNITS) {
         const int row = k0 + u / KCH, c = u % KCH;
         const uint32_t off = row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes;
-        kreg[i] = ld128(rk, off);
+        stg[i] = ld128(rk, off);
       }
     }
     if (is_yat(VAR) && gtid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * gtid);
@@ -199,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
       if (u < K_UNITS) {
         const int j = u / KCH, c = u % KCH;
         const int row = (j & ~31) | k_lds_row(j & 31);
-        *(u32x4*)&K[row * KLD + 8 * c] = kreg[i];
+        *(u32x4*)&K[row * KLD + 8 * c] = stg[i];
       }
     }
     if (is_yat(VAR) && gtid < BN / 4) *(f32x4*)&sNK[t % 3][4 * gtid] = nkreg;
@@ -214,7 +262,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
         for (int r = 0; r < 4; ++r) {
           const int row = k0 + 4 * g4 + r;
           const uint32_t off = row < p.Tk ? (uint32_t)((row * vst + 8 * c) * 2) : v_bytes;
-          vreg[i][r] = ld128(rv, off);
+          stg[4 * i + r] = ld128(rv, off);
         }
       }
     }
@@ -229,8 +277,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
         // 4 keys x 8 values -> 8 value rows of 4 keys each.
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
-          const unsigned a2 = vreg[i][2][e], a3 = vreg[i][3][e];
+          const unsigned a0 = stg[4 * i][e], a1 = stg[4 * i + 1][e];
+          const unsigned a2 = stg[4 * i + 2][e], a3 = stg[4 * i + 3][e];
           u32x2 lo, hi;
           lo[0] = (a0 & 0xffffu) | (a1 << 16);
           lo[1] = (a2 & 0xffffu) | (a3 << 16);
@@ -271,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           bf16x8, *(const u32x4*)&K[(kb * 32 + col) * KLD + 16 * s + 8 * half]);
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = sinit;
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       const int s = i / KB, kb = i % KB;
@@ -377,7 +425,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           for (int r = 0; r < 8; ++r) rc[r] = __builtin_amdgcn_rcpf(den[r]);
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            const float u = sacc[kb][r0 + r] + bias;
+            const float u = sacc[kb][r0 + r];  // q.k + b
             float kap = yat_numerator<VAR>(u, p.yat_power) * rc[r];
             if (MASK) kap = allowed(kb, r0 + r) ? kap : 0.f;
             sacc[kb][r0 + r] = kap;
@@ -555,7 +603,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // Per-head scalars (prologue).
   float bias = 0.f, eps = 0.f, tau = 0.f;
   if (is_yat(VAR)) {
-    bias = p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
+    bias = yat_bias(p, h);
     eps = softplus_precise(p.eps_raw[h]);
   } else if (VAR == kStau) {
     tau = softplus_precise(p.log_tau[h]) + 1.f;
@@ -572,12 +620,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     __builtin_amdgcn_s_waitcnt(0);  // not outstanding on entry to the main loop
   }
   float nq = 0.f;
-  // |k|^2 slice of this key/value head; padded to a multiple of 64 rows, so a
+  // |k|^2 + b slice of this query head; padded to a multiple of 64 rows, so a
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
-      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;
+  const f32x16 sinit = score_init<VAR>(bias);
+  const int b_sgpr = __builtin_amdgcn_readfirstlane(__float_as_int(bias));
   if (is_yat(VAR)) {
-    f32x16 g = {};
+    f32x16 g = sinit;
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
     if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
@@ -672,8 +722,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 
     // S^T = K Q^T, the KB accumulation chains interleaved.
     f32x16 sacc[KB];
+    if constexpr (is_yat(VAR)) {
+      // the start values are rebuilt from a scalar for every tile (holding
+      // them across the loop would cost 16 registers)
+      int b_bits = b_sgpr;
+      asm volatile("" : "+s"(b_bits));
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = __int_as_float(b_bits);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -739,9 +800,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sacc[kb][r];
-          const float d2 = fmaf(-2.f, s, nq + nk[r]);
-          const float u = s + bias;
+          const float u = sacc[kb][r];  // q.k + b
+          const float d2 = fmaf(-2.f, u, nq + nk[r]);
           float kap = yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
           if (MASK) kap = allowed(kb, r) ? kap : 0.f;
           sacc[kb][r] = kap;
@@ -1091,11 +1151,9 @@ template <int VAR, int DV>
 hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   constexpr int DK = SFS_DK;
   constexpr int BN = SFS_BN;
-  if (is_yat(VAR)) {
-    const dim3 grid((p.Tk + 127) / 128, p.Hkv, p.B);
-    hipLaunchKernelGGL(row_norms_bf16<DK>, grid, dim3(256), 0, stream,
-                       (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk, p.nk);
-  }
+  if (is_yat(VAR))
+    hipLaunchKernelGGL(yat_key_norms_bf16<DK>, dim3((p.Tk + 127) / 128, p.Hq, p.B), dim3(256), 0,
+                       stream, p);
   // p.block_rows and p.kv_splits come from the host plan (make_plan)
   const unsigned bh = (unsigned)p.B * (unsigned)p.Hq;
   const unsigned nq = (unsigned)((p.Tq + p.block_rows - 1) / p.block_rows) * bh;

@@ -617,7 +617,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   if (my_q < p.Tq) {
     const int64_t idx = row_idx;
     if (!DELTA) D = p.row_d[idx];
-    Z = p.row_z[idx];
+    // Yat's D pass forms the normaliser itself (below): its weights are kappa
+    Z = DELTA && is_yat(VAR) ? 1.f : p.row_z[idx];
     if (is_yat(VAR)) nq = p.nq[idx];
   }
   const HeadC hc = head_consts<VAR, DK>(p, h);
@@ -678,7 +679,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   for (int i = 0; i < KB; ++i) accQ[i] = f32x16{};
   float corr = 0.f;            // Yat: sum over the lane's keys of B'/2 = bf16(g/2) - A/2
   float sum0 = 0.f, sum1 = 0.f;  // Yat: sum A/2, sum B/2; s^tau: sum w (dp - D) log2(phi)
-  float dsum = 0.f;            // DELTA: sum over the lane's keys of w dp
+  float dsum = 0.f;            // DELTA: sum over the lane's keys of w dp (Yat: kappa dp)
+  float msum = 0.f;            // DELTA, Yat: sum over the lane's keys of kappa
 
   // Scores of one tile -> packed gradient scores (pg) and the row sums.
   auto scores = [&](auto mask_tag, int buf, int k0, u32x4* pg) {
@@ -711,8 +713,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
           const int kj = k0 + k8 + e;
           const bool ok = !MASK || (my_q < p.Tq && kj < p.Tk && !(p.causal && kj > my_q));
           if (DELTA) {
-            const float wv = pair_weight<VAR>(sacc[r], Z, nq + nkv, hc);
-            dsum = fmaf(ok ? wv : 0.f, pacc[r], dsum);
+            const float wv = ok ? pair_weight<VAR>(sacc[r], Z, nq + nkv, hc) : 0.f;
+            dsum = fmaf(wv, pacc[r], dsum);
+            if (is_yat(VAR)) msum += wv;
             gv[o] = av[o] = lv[o] = 0.f;
           } else {
             pair_grad<VAR>(sacc[r], pacc[r], D, Z, nq + nkv, hc, gv[o], av[o], lv[o]);
@@ -770,7 +773,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 
   if (DELTA) {
     dsum = pair_sum(dsum);
-    if (my_q < p.Tq && half == 0) p.row_d[row_idx] = dsum;
+    if (is_yat(VAR)) {
+      // Z = 1 / (sum_j kappa_ij + 1e-9) from these same kappa, so that a row's
+      // weights add to mass / (mass + 1e-9) in this evaluation's rounding and
+      // dp - D cancels where the exact gradient does (a row whose weight sits
+      // on one key), whatever rounding the forward's kappa took
+      const float z = 1.f / (pair_sum(msum) + 1e-9f);
+      if (my_q < p.Tq && half == 0) {
+        p.row_z[row_idx] = z;
+        p.row_d[row_idx] = dsum * z;
+      }
+    } else if (my_q < p.Tq && half == 0) {
+      p.row_d[row_idx] = dsum;
+    }
     return;
   }
 

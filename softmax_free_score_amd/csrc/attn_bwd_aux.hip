@@ -3,12 +3,13 @@
 // bwd_rows: for every query row i the normaliser the forward divided by,
 // which every pair (i, j) of the gradient kernels needs:
 //   d L / d u_ij = (dout_i . v_j - D_i) / Z_i   for w_ij = u_ij / Z_i.
-// Z_i is mass + 1e-9 for Yat ("Softmax-Free Attention in JAX/Flax NNX", "One
-// module, two compatibility functions"), the mass for s^tau ("s^tau" forum
-// post, core formula), and for softmax the weights are exp2(s_ij log2(e) -
-// L_i) with L_i = log2(sum_j e^(s_ij - max_i)) + max_i log2(e).  Also clears
-// D (the row sums sum_j w_ij dp_ij that the first pass of attn_bwd.hip fills
-// in), padding included.
+// Z_i is the mass for s^tau ("s^tau" forum post, core formula), and for
+// softmax the weights are exp2(s_ij log2(e) - L_i) with L_i = log2(sum_j
+// e^(s_ij - max_i)) + max_i log2(e).  Yat's 1 / (mass + 1e-9) ("Softmax-Free
+// Attention in JAX/Flax NNX", "One module, two compatibility functions") is
+// formed by the first pass of attn_bwd.hip from its own kappa; here it is
+// cleared.  Also clears D (the row sums sum_j w_ij dp_ij that the first pass
+// fills in), padding included.
 //
 // bwd_params: per query head, the parameter gradients from the per-workgroup
 // sums of the dq kernel, added in a fixed order in fp64:
@@ -34,10 +35,8 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdProblem p) {
   float z = 0.f;
   if (i < p.Tq) {
     const int64_t ri = bh * p.Tq + i;
-    const float m = p.mass[ri];
-    if (is_yat(p.variant)) z = 1.f / (m + 1e-9f);
-    else if (p.variant == kSoftmax) z = fmaf(p.max_score[ri], kLog2eF, log2f(m));
-    else z = m > 0.f ? 1.f / m : 0.f;
+    if (p.variant == kSoftmax) z = fmaf(p.max_score[ri], kLog2eF, log2f(p.mass[ri]));
+    else if (p.variant == kStau) z = p.mass[ri] > 0.f ? 1.f / p.mass[ri] : 0.f;
   }
   p.row_d[r] = 0.f;
   p.row_z[r] = z;

@@ -92,7 +92,8 @@ struct Problem {
   const float* b_raw;
   const float* eps_raw;
   const float* log_tau;
-  float* nk;         // Yat: |k_j|^2 per key row [B*Hkv][nk_pitch(Tk)] (workspace)
+  float* nk;         // Yat (workspace): forward |k_j|^2 + b_h [B*Hq][nk_pitch(Tk)];
+                     // telemetry |k_j|^2 [B*Hkv][nk_pitch(Tk)]
   int64_t qs[3], ks[3], vs[3], os[3];  // element strides for (b, h, t)
   int B, Hq, Hkv, Tq, Tk, dk, dv;
   int variant;

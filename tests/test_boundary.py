@@ -113,7 +113,7 @@ def test_workspace_rules():
     lib = attn.load_library()
     d = desc(B=2, Hq=4, Hkv=2, Tq=100, Tk=100)
     need = lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_YAT)
-    assert need == 2 * 2 * 128 * 4                   # |k|^2 rows padded to 64
+    assert need == 2 * 4 * 128 * 4                   # |k|^2 + b per query head, rows padded to 64
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_SOFTMAX) == 0
     assert lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_STAU) == 0
     assert lib.attn_fwd_workspace_bytes(None, attn.ATTN_YAT) == 0
@@ -190,7 +190,7 @@ def test_workspace_bytes_with_splits():
     assert ws(d, attn.ATTN_SOFTMAX) == 0
     d.kv_splits = 3                                   # 3 chunks x 16 rows x (128 + 4) floats
     assert ws(d, attn.ATTN_SOFTMAX) == 3 * 16 * 132 * 4
-    nk = 2 * 2 * 4096 * 4                             # Yat: |k|^2 rows first (256-aligned)
+    nk = 2 * 8 * 4096 * 4                             # Yat: |k|^2 + b rows first (256-aligned)
     assert ws(d, attn.ATTN_YAT) == nk + 3 * 16 * 132 * 4
     d.dtype = attn.ATTN_F32
     assert ws(d, attn.ATTN_SOFTMAX) == 0
@@ -249,6 +249,8 @@ def test_bwd_validation():
         assert call_bwd(desc(), **{kw: 0}) == ERR_NULL, kw
     assert call_bwd(desc(), mx=0) == ERR_NULL                        # softmax needs max_score
     assert call_bwd(desc(), variant=attn.ATTN_YAT, mx=0) == ERR_HIP  # Yat does not
+    assert call_bwd(desc(), variant=attn.ATTN_YAT, mass=0, mx=0) == ERR_HIP  # nor the mass
+    assert call_bwd(desc(), variant=attn.ATTN_STAU, mass=0) == ERR_NULL
     assert call_bwd(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
     assert call_bwd(desc(), variant=attn.ATTN_STAU, lt=0) == ERR_PARAM
     # parameter gradients are optional

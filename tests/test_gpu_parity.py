@@ -214,6 +214,22 @@ def test_decode_kernel_tied_and_yat_options():
         full_check(inp, "yat", False, "decode_yat_opts", block_rows=(8,), yat_opts=opts)
 
 
+@pytest.mark.parametrize("shape,rows", [
+    ((2, 4, 4, 200, 200, 128, 128), BLOCK_ROWS),     # every tile kernel
+    ((1, 2, 2, 100, 100, 64, 32), BLOCK_ROWS),
+    ((1, 4, 4, 2, 2, 128, 128), (8,)),               # the decode kernel
+])
+def test_yat_tied_keys_with_tiny_eps(shape, rows):
+    """k := q and eps = softplus(-20) ~ 2e-9: the diagonal weight is
+    (|q|^2 + b)^2 / eps only if the kernel's d2 = |q|^2 + |k|^2 - 2 q.k is
+    exactly 0 there (a residual of one rounding unit of |q|^2 would shrink it
+    by orders of magnitude), so mass and max_score pin that cancellation."""
+    B, Hq, Hkv, Tq, Tk, dk, dv = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", True, seed=26, qk_std=1.5, tied=True)
+    inp.eps_raw = np.full_like(inp.eps_raw, -20.0)
+    full_check(inp, "yat", True, "yat_tied_tiny_eps", block_rows=rows)
+
+
 def test_kv_splits_more_chunks_than_tiles():
     # 64 chunks over 4 tiles of keys: most chunks are empty and write neutral partials
     inp = make_custom(1, 2, 2, 40, 100, 64, 64, "bf16", False, seed=21)
