@@ -40,13 +40,18 @@ def alg_flops(wl) -> float:
     return float(wl.allowed_pairs) * 2.0 * (wl.dk + wl.dv)
 
 
-def kernels_timed(wl, args, variant) -> str:
-    """The kernels one timed forward call runs, by the library's plan: the
-    decode kernel and its merge when a key/value head has at most 8 query
-    rows (or block_rows = 8 forces it), else the fused tile kernel, after the
-    |k|^2 pre-pass for Yat."""
+def uses_decode_kernel(wl, args) -> bool:
+    """The library's plan: the decode kernel runs when a key/value head has
+    at most 8 query rows and no launch option overrides it, or when
+    block_rows = 8 forces it."""
     packed = wl.Hq // wl.Hkv * wl.Tq
-    if args.block_rows == 8 or (args.block_rows == 0 and args.kv_splits == 0 and packed <= 8):
+    return args.block_rows == 8 or (args.block_rows == 0 and args.kv_splits == 0 and packed <= 8)
+
+
+def kernels_timed(wl, args, variant) -> str:
+    """The kernels one timed forward call runs: the decode kernel and its
+    merge, or the fused tile kernel after the |k|^2 pre-pass for Yat."""
+    if uses_decode_kernel(wl, args):
         return f"attn_decode_bf16 ({variant}) + combine_partials"
     pre = "|k|^2 pre-pass + " if variant == "yat" else ""
     return f"{pre}attn_fwd_bf16 ({variant})"
@@ -62,21 +67,24 @@ def alg_bytes(wl) -> float:
 
 
 # sources the fused forward kernel is compiled from
-KERNEL_SOURCES = [os.path.join(ROOT, "softmax_free_score_amd", "csrc", f)
-                  for f in ("attn_bf16.hip", "bf16_common.h", "attn_launch.h")]
+# sources of the dominant kernel: the fused tile kernels, or the decode kernel
+KERNEL_SOURCES = {
+    False: ("attn_bf16.hip", "bf16_common.h", "attn_launch.h"),
+    True: ("attn_decode.hip", "bf16_common.h", "attn_launch.h"),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(decode: bool = False) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[decode]:
+        with open(os.path.join(ROOT, "softmax_free_score_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, variant: str):
-    """HBM bytes per launch of the fused kernel from the committed counter
+def recorded_traffic(workload: str, variant: str, decode: bool = False):
+    """HBM bytes per launch of the dominant kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a
     plain copy of known size), or None when there is none for this workload and
     variant or the kernel source changed since the counters were taken."""
@@ -86,7 +94,7 @@ def recorded_traffic(workload: str, variant: str):
     except (OSError, ValueError):
         return None
     r = rec.get(f"{workload}/{variant}")
-    if not r or r.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not r or r.get("kernel_source_sha256_16") != kernel_source_hash(decode):
         return None
     return r.get("bytes_per_launch")
 
@@ -250,8 +258,10 @@ def main():
                    "kv_splits": args.kv_splits,
                    "parallelism": "none (1 GPU)"},
         "roofline": {**roof,
-                     "traffic": recorded_traffic(wl.name, primary),
-                     "traffic_unit": "bytes per launch of attn_fwd_bf16 (HBM, counters)",
+                     "traffic": recorded_traffic(wl.name, primary, uses_decode_kernel(wl, args)),
+                     "traffic_unit": "bytes per launch of "
+                                     f"{'attn_decode_bf16' if uses_decode_kernel(wl, args) else 'attn_fwd_bf16'}"
+                                     " (HBM, counters)",
                      "kernel": f"{kernels_timed(wl, args, primary)}; flops = "
                                f"{flops:.4e} per launch ({wl.allowed_pairs} allowed pairs x "
                                f"2(dk+dv))",
@@ -266,7 +276,7 @@ def main():
         # > 1 means the primary branch is faster than softmax on the same inputs
         line[f"{primary}_speed_vs_softmax"] = round(others["softmax"]["ms"] / mean_ms, 4)
     line["roofline"]["alg_bytes_per_launch"] = alg_bytes(wl)
-    line["kernel_source_sha256_16"] = kernel_source_hash()
+    line["kernel_source_sha256_16"] = kernel_source_hash(uses_decode_kernel(wl, args))
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
