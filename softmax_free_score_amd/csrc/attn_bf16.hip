@@ -280,10 +280,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           const unsigned a0 = stg[4 * i][e], a1 = stg[4 * i + 1][e];
           const unsigned a2 = stg[4 * i + 2][e], a3 = stg[4 * i + 3][e];
           u32x2 lo, hi;
-          lo[0] = (a0 & 0xffffu) | (a1 << 16);
-          lo[1] = (a2 & 0xffffu) | (a3 << 16);
-          hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+          lo[0] = lo_halves(a0, a1);
+          lo[1] = lo_halves(a2, a3);
+          hi[0] = hi_halves(a0, a1);
+          hi[1] = hi_halves(a2, a3);
           *(u32x2*)&Vt[(8 * c + 2 * e) * VLD + 4 * g4] = lo;
           *(u32x2*)&Vt[(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
         }
@@ -694,10 +694,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
           const unsigned a2 = vreg[i][2][e], a3 = vreg[i][3][e];
           u32x2 lo, hi;
-          lo[0] = (a0 & 0xffffu) | (a1 << 16);
-          lo[1] = (a2 & 0xffffu) | (a3 << 16);
-          hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+          lo[0] = lo_halves(a0, a1);
+          lo[1] = lo_halves(a2, a3);
+          hi[0] = hi_halves(a0, a1);
+          hi[1] = hi_halves(a2, a3);
           *(u32x2*)&sV[buf][(8 * c + 2 * e) * VLD + 4 * g4] = lo;
           *(u32x2*)&sV[buf][(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
         }

@@ -319,10 +319,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
     for (int e = 0; e < 4; ++e) {
       const unsigned a0 = rows[0][e], a1 = rows[1][e], a2 = rows[2][e], a3 = rows[3][e];
       u32x2 lo, hi;
-      lo[0] = (a0 & 0xffffu) | (a1 << 16);
-      lo[1] = (a2 & 0xffffu) | (a3 << 16);
-      hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-      hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+      lo[0] = lo_halves(a0, a1);
+      lo[1] = lo_halves(a2, a3);
+      hi[0] = hi_halves(a0, a1);
+      hi[1] = hi_halves(a2, a3);
       *(u32x2*)&Tr[(8 * c + 2 * e) * TLD + 4 * g4] = lo;
       *(u32x2*)&Tr[(8 * c + 2 * e + 1) * TLD + 4 * g4] = hi;
     }

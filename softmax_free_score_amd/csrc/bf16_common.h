@@ -38,6 +38,14 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(unsigned, v);
 }
+// Two bf16 words from two packed pairs, one byte permute each: the low
+// halves of a and b (a's in the low half of the result), or the high halves.
+__device__ __forceinline__ unsigned lo_halves(unsigned a, unsigned b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ unsigned hi_halves(unsigned a, unsigned b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
 // log(1 + e^x) without overflow (fp32 library calls; used once per head).
 __device__ __forceinline__ float softplus_precise(float x) {
   return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
