@@ -227,14 +227,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   u32x4 stg[NSTG];
   f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
 
+  // Tile loads.  A tile wholly inside T_k takes plain offsets (one add per
+  // load); the last, partial tile points its rows >= T_k past the slice, where
+  // buffer loads return 0.
   auto load_k = [&](int k0) {
+    // this thread's rows are k0 + u / KCH for u = gtid + i GT: one base
+    // offset, then steps of (GT / KCH) rows
+    const uint32_t off0 = (uint32_t)(((k0 + gtid / KCH) * kst + 8 * (gtid % KCH)) * 2);
+    const uint32_t step = (uint32_t)((GT / KCH) * kst * 2);
+    if (k0 + BN <= p.Tk) {  // uniform
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int u = gtid + i * GT;
-      if (u < K_UNITS) {
-        const int row = k0 + u / KCH, c = u % KCH;
-        const uint32_t off = row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes;
-        stg[i] = ld128(rk, off);
+      for (int i = 0; i < K_PER_T; ++i)
+        if (gtid + i * GT < K_UNITS) stg[i] = ld128(rk, off0 + i * step);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K_PER_T; ++i) {
+        const int row = k0 + (gtid + i * GT) / KCH;
+        if (gtid + i * GT < K_UNITS) stg[i] = ld128(rk, row < p.Tk ? off0 + i * step : k_bytes);
       }
     }
     if (is_yat(VAR) && gtid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * gtid);
@@ -253,16 +262,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
     if (is_yat(VAR) && gtid < BN / 4) *(f32x4*)&sNK[t % 3][4 * gtid] = nkreg;
   };
   auto load_v = [&](int k0) {
+    const bool full = k0 + BN <= p.Tk;  // uniform
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = gtid + i * GT;
       if (u < V_UNITS) {
         const int g4 = u % (BN / 4), c = u / (BN / 4);
+        const uint32_t off0 = (uint32_t)(((k0 + 4 * g4) * vst + 8 * c) * 2);
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = k0 + 4 * g4 + r;
-          const uint32_t off = row < p.Tk ? (uint32_t)((row * vst + 8 * c) * 2) : v_bytes;
-          stg[4 * i + r] = ld128(rv, off);
+          for (int r = 0; r < 4; ++r) stg[4 * i + r] = ld128(rv, off0 + (uint32_t)(r * vst * 2));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            stg[4 * i + r] = ld128(rv, k0 + 4 * g4 + r < p.Tk ? off0 + (uint32_t)(r * vst * 2)
+                                                               : v_bytes);
         }
       }
     }
@@ -647,26 +661,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   u32x4 vreg[V_PER_T][4];
   f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
 
+  // A tile wholly inside T_k takes plain offsets (one add per load); the
+  // last, partial tile points its rows >= T_k past the slice (loads give 0).
+  static_assert(NT % KCH == 0 && NT % (BN / 4) == 0, "load offsets step evenly");
   auto load_tile = [&](int k0) {
+    const bool full = k0 + BN <= p.Tk;
+    const uint32_t koff = (uint32_t)(((k0 + tid / KCH) * kst + 8 * (tid % KCH)) * 2);
+    const uint32_t kstep = (uint32_t)((NT / KCH) * kst * 2);
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (u < K_UNITS) {
-        const int row = k0 + u / KCH, c = u % KCH;
-        const uint32_t off = row < p.Tk ? (uint32_t)((row * kst + 8 * c) * 2) : k_bytes;
-        kreg[i] = ld128(rk, off);
+      if (tid + i * NT < K_UNITS) {
+        const int row = k0 + (tid + i * NT) / KCH;
+        kreg[i] = ld128(rk, full || row < p.Tk ? koff + i * kstep : k_bytes);
       }
     }
+    const int g4 = tid % (BN / 4);
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (u < V_UNITS) {
-        const int g4 = u % (BN / 4), c = u / (BN / 4);
+      if (tid + i * NT < V_UNITS) {
+        const int c = (tid + i * NT) / (BN / 4);
+        const uint32_t voff = (uint32_t)(((k0 + 4 * g4) * vst + 8 * c) * 2);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = k0 + 4 * g4 + r;
-          const uint32_t off = row < p.Tk ? (uint32_t)((row * vst + 8 * c) * 2) : v_bytes;
-          vreg[i][r] = ld128(rv, off);
+          vreg[i][r] = ld128(rv, full || row < p.Tk ? voff + (uint32_t)(r * vst * 2) : v_bytes);
         }
       }
     }
