@@ -178,6 +178,51 @@ __device__ __forceinline__ void pair_grad(float sd, float dp, float D, float Z, 
   }
 }
 
+// The forward's weight of one pair (as pair_weight) together with the factor
+// the dK wave's gradient score needs from the same evaluation, so that the
+// map runs once per pair in attn_bwd_kv:
+//   Yat     mult = u r:                  A/2 = (dp - D) Z mult, g/2 = A/2 (1 + mult);
+//   softmax mult = w:                    g = mult (dp - D);
+//   s^tau   mult = w tau sigmoid(s)/phi: g = mult (dp - D).
+template <int VAR>
+__device__ __forceinline__ float pair_weight_mult(float sd, float Z, float nqk, const HeadC& hc,
+                                                  float& mult) {
+  if constexpr (is_yat(VAR)) {
+    const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
+    const float u = sd + hc.bias;
+    const float ur = u * rden;
+    mult = ur;
+    return u * ur * Z;
+  } else if constexpr (VAR == kSoftmax) {
+    const float w = __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
+    mult = w;
+    return w;
+  } else {
+    const float s = sd * hc.scale;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+    const float u1 = 1.f + e;
+    const float c = (u1 - 1.f) - e;
+    const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
+    const float phi = sp + 1e-6f;
+    const float w = __builtin_amdgcn_exp2f(hc.tau * __builtin_amdgcn_logf(phi)) * Z;
+    const float sig = (s >= 0.f ? 1.f : e) * __builtin_amdgcn_rcpf(u1);  // sigmoid(s)
+    mult = w * hc.tau * sig * __builtin_amdgcn_rcpf(phi);
+    return w;
+  }
+}
+// The gradient score from that factor; Yat returns g/2 and sets a = A/2.
+template <int VAR>
+__device__ __forceinline__ float grad_from_mult(float mult, float dp, float D, float Z,
+                                                float& a) {
+  if constexpr (is_yat(VAR)) {
+    a = (dp - D) * Z * mult;
+    return fmaf(a, mult, a);
+  } else {
+    a = 0.f;
+    return mult * (dp - D);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV: 8 waves in 4 pairs; pair p owns keys k0 + 32 p .. k0 + 32 p + 31 of
 // one (b, kv head) and streams 32-query tiles of every query head of the
@@ -187,12 +232,15 @@ __device__ __forceinline__ void pair_grad(float sd, float dp, float D, float Z, 
 // share a SIMD without spilling, and each issues 16 of a tile's 32 MFMAs.
 // The two are pipelined one tile apart, one barrier per tile:
 //
-//   iteration t:  A: weights of tile t from S_t (its registers), dV^T += dO^T P,
-//                    S_{t+1} = Q_{t+1} K^T -> registers and LDS
-//                 B: dP_t = dO_t V^T, S_t <- LDS, gradient scores, dK^T += Q^T G
+//   iteration t:  A: dV^T += dO_t^T P_t (P_t in its registers), S_{t+1} =
+//                    Q_{t+1} K^T, the weights P_{t+1} -> registers and, per
+//                    pair, the factor of B's gradient score -> LDS
+//                 B: dP_t = dO_t V^T, the factors of tile t <- LDS, gradient
+//                    scores, dK^T += Q^T G
 //
 // so on each SIMD one wave's matrix-core work overlaps the other's vector
-// work.  Tiles live in three LDS stages: tile t is read in iteration t (and
+// work, and the score -> weight map is evaluated once per pair (B's terms
+// are two or three products of A's factor).  Tiles live in three LDS stages: tile t is read in iteration t (and
 // its Q rows already in t - 1), tile t + 2 is written in iteration t from
 // registers loaded in iteration t - 1.
 template <int VAR, int DK, int DV>
@@ -344,48 +392,98 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
       sNQ[slot][tid] = st_nq;
     }
   };
-  // A: S = Q K^T of the tile in `slot`, kept in registers and handed to B.
-  auto scores = [&](int slot, int ss, f32x16& sacc) {
-    sacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQ[slot][col * QLD + 16 * s + 8 * half]),
-                    frag[s], sacc);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      sS[ss][pr][m][lane] = f32x4{sacc[4 * m], sacc[4 * m + 1], sacc[4 * m + 2], sacc[4 * m + 3]};
-  };
   // a tile whose every query precedes every key of this pair: nothing to do
   auto active = [&](int qt) { return !(p.causal && qt * BQ + BQ - 1 < kw); };
+  auto needs_mask = [&](int qb) { return (p.causal && qb < kw + 32) || qb + BQ > p.Tq; };
 
   // A: dV^T; B: dK^T (rows are value / key columns, the keys are the columns)
   f32x16 acc[AB];
 #pragma unroll
   for (int i = 0; i < AB; ++i) acc[i] = f32x16{};
   float corr = 0.f;  // B, Yat: sum over the lane's queries of B'/2 = bf16(g/2) - A/2
-  HeadC hc{};
+  HeadC hc{};        // A: constants of query head hk g + hc_gi, the head last mapped
+  int hc_gi = -1;
 
-  // The per-pair terms of one tile from S (sacc) and, in B, dP (pacc); then
-  // A: dV^T += dO^T P, B: dK^T += Q^T G.  ROLE_A is the wave's role, so each
-  // wave computes only its own terms.
-  auto terms = [&](auto mask_tag, auto role_tag, int slot, int qb, const f32x16& sacc,
-                   const f32x16& pacc) {
+  // A: S = Q K^T of the tile in `slot`, its weights packed to bf16 into pk
+  // and B's factors into sS[ss].  Masked pairs get weight and factor 0.
+  auto weights = [&](auto mask_tag, int slot, int ss, int qb, u32x4* pk) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool ROLE_A = decltype(role_tag)::value;
-    u32x4 pk[2];
+    f32x16 sacc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQ[slot][col * QLD + 16 * s + 8 * half]),
+                    frag[s], sacc);
+    f32x16 mult;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // accumulator elements 8 s .. 8 s + 7: queries qb + 16 s + 8 half + 0..7
       const int q8 = 16 * s + 8 * half;
-      f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, n0 = d0, n1 = d0;
-      if (!ROLE_A) {
-        d0 = *(const f32x4*)&sD[slot][q8];
-        d1 = *(const f32x4*)&sD[slot][q8 + 4];
-      }
+      f32x4 n0 = {0.f, 0.f, 0.f, 0.f}, n1 = n0;
       const f32x4 z0 = *(const f32x4*)&sZ[slot][q8], z1 = *(const f32x4*)&sZ[slot][q8 + 4];
       if (is_yat(VAR)) {
         n0 = *(const f32x4*)&sNQ[slot][q8];
         n1 = *(const f32x4*)&sNQ[slot][q8 + 4];
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float v[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int e = 2 * e2 + o, r = 8 * s + e;
+          const float Z = e < 4 ? z0[e] : z1[e - 4];
+          const float nq = e < 4 ? n0[e] : n1[e - 4];
+          float m;
+          v[o] = pair_weight_mult<VAR>(sacc[r], Z, nq + nk, hc, m);
+          if (MASK) {
+            const int qi = qb + q8 + e;
+            const bool ok = qi < p.Tq && !(p.causal && my_k > qi);
+            v[o] = ok ? v[o] : 0.f;
+            m = ok ? m : 0.f;
+          }
+          mult[r] = m;
+        }
+        pk[s][e2] = pack_bf16(v[0], v[1]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      sS[ss][pr][m][lane] = f32x4{mult[4 * m], mult[4 * m + 1], mult[4 * m + 2], mult[4 * m + 3]};
+  };
+  // A: dV^T += dO^T P of the tile in `slot`.
+  auto dv_update = [&](int slot, const u32x4* pk) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, pk[s]);
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sOt[slot][(32 * i + col) * TLD + 16 * s + 8 * half]),
+                        bop, acc[i]);
+    }
+  };
+  // B: dP of the tile in `slot`, A's factors from sS[ss], the gradient scores
+  // G and dK^T += Q^T G.  (Masked pairs have factor 0, hence G = 0.)
+  auto grads = [&](int slot, int ss) {
+    f32x16 pacc = {};
+#pragma unroll
+    for (int s = 0; s < VS; ++s)
+      pacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sO[slot][col * OLD + 16 * s + 8 * half]),
+                    frag[s], pacc);
+    f32x16 mult;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 x = sS[ss][pr][m][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mult[4 * m + e] = x[e];
+    }
+    u32x4 pk[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int q8 = 16 * s + 8 * half;
+      const f32x4 d0 = *(const f32x4*)&sD[slot][q8], d1 = *(const f32x4*)&sD[slot][q8 + 4];
+      f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;
+      if (is_yat(VAR)) {
+        z0 = *(const f32x4*)&sZ[slot][q8];
+        z1 = *(const f32x4*)&sZ[slot][q8 + 4];
       }
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -395,42 +493,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
           const int e = 2 * e2 + o, r = 8 * s + e;
           const float D = e < 4 ? d0[e] : d1[e - 4];
           const float Z = e < 4 ? z0[e] : z1[e - 4];
-          const float nq = e < 4 ? n0[e] : n1[e - 4];
-          if (ROLE_A) {
-            v[o] = pair_weight<VAR>(sacc[r], Z, nq + nk, hc);
-            av[o] = 0.f;
-          } else {
-            float lt;
-            pair_grad<VAR>(sacc[r], pacc[r], D, Z, nq + nk, hc, v[o], av[o], lt);
-          }
-          if (MASK) {
-            const int qi = qb + q8 + e;
-            const bool ok = qi < p.Tq && !(p.causal && my_k > qi);
-            v[o] = ok ? v[o] : 0.f;
-            av[o] = ok ? av[o] : 0.f;
-          }
+          v[o] = grad_from_mult<VAR>(mult[r], pacc[r], D, Z, av[o]);
         }
         pk[s][e2] = pack_bf16(v[0], v[1]);
-        if (!ROLE_A && is_yat(VAR))
+        if (is_yat(VAR))
           corr += (bf16_lo(pk[s][e2]) - av[0]) + (bf16_hi(pk[s][e2]) - av[1]);
       }
     }
-    const unsigned short* T = ROLE_A ? sOt[slot] : sQt[slot];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const bf16x8 bop = __builtin_bit_cast(bf16x8, pk[s]);
 #pragma unroll
-      for (int i = 0; i < (ROLE_A ? VB : KB); ++i)
-          acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&T[(32 * i + col) * TLD + 16 * s + 8 * half]),
-                          bop, acc[i]);
+      for (int i = 0; i < KB; ++i)
+        acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQt[slot][(32 * i + col) * TLD + 16 * s + 8 * half]),
+                        bop, acc[i]);
     }
   };
+  // A: S, weights and factors of the tile at `x` in `slot`
+  auto map_tile = [&](Pos x, int slot, int ss, u32x4* pk) {
+    const int qb = x.qt * BQ;
+    if (needs_mask(qb)) weights(std::true_type{}, slot, ss, qb, pk);
+    else weights(std::false_type{}, slot, ss, qb, pk);
+  };
 
-  // Prologue: tiles 0 and 1 into their stages, tile 2 into registers, S_0.
+  // Prologue: tiles 0 and 1 into their stages, tile 2 into registers; A maps
+  // tile 0.
   Pos cur{0, qt0};       // tile it
   Pos nxt = cur;         // tile it + 1
   Pos ld = cur;          // next tile to load
-  f32x16 s_cur = {};     // A: S of tile it
+  u32x4 pk_cur[2] = {};  // A: P of tile it in bf16
   if (n_it > 0) {
     load(ld);
     store(0);
@@ -447,7 +538,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   }
   advance(nxt);
   __syncthreads();
-  if (n_it > 0 && is_a && active(cur.qt)) scores(0, 0, s_cur);
+  if (n_it > 0 && is_a && active(cur.qt)) {
+    hc = head_consts<VAR, DK>(p, hk * g + cur.gi);
+    hc_gi = cur.gi;
+    map_tile(cur, 0, 0, pk_cur);
+  }
   __syncthreads();
 
   for (int it = 0; it < n_it; ++it) {
@@ -458,32 +553,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
       load(ld);
       advance(ld);
     }
-    const int qb = cur.qt * BQ;
-    if (it == 0 || cur.qt == qt0) hc = head_consts<VAR, DK>(p, hk * g + cur.gi);
     const bool act = active(cur.qt);
-    const bool need_mask = (p.causal && qb < kw + 32) || qb + BQ > p.Tq;
     if (is_a) {
-      if (act) {
-        const f32x16 none = {};
-        if (need_mask) terms(std::true_type{}, std::true_type{}, slot, qb, s_cur, none);
-        else terms(std::false_type{}, std::true_type{}, slot, qb, s_cur, none);
+      if (act) dv_update(slot, pk_cur);
+      if (it + 1 < n_it && active(nxt.qt)) {
+        if (nxt.gi != hc_gi) {
+          hc = head_consts<VAR, DK>(p, hk * g + nxt.gi);
+          hc_gi = nxt.gi;
+        }
+        u32x4 pk_nxt[2];
+        map_tile(nxt, (it + 1) % NS, (it + 1) & 1, pk_nxt);
+        pk_cur[0] = pk_nxt[0];
+        pk_cur[1] = pk_nxt[1];
       }
-      if (it + 1 < n_it && active(nxt.qt)) scores((it + 1) % NS, (it + 1) & 1, s_cur);
     } else if (act) {
-      f32x16 pacc = {};
-#pragma unroll
-      for (int s = 0; s < VS; ++s)
-        pacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sO[slot][col * OLD + 16 * s + 8 * half]),
-                      frag[s], pacc);
-      f32x16 sacc;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 x = sS[it & 1][pr][m][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[4 * m + e] = x[e];
-      }
-      if (need_mask) terms(std::true_type{}, std::false_type{}, slot, qb, sacc, pacc);
-      else terms(std::false_type{}, std::false_type{}, slot, qb, sacc, pacc);
+      grads(slot, it & 1);
     }
     cur = nxt;
     advance(nxt);
