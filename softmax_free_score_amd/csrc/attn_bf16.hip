@@ -1069,7 +1069,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128),
     if (is_yat(VAR) && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
   };
 
-  float ent = 0.f, n_sparse = 0.f, n_allowed = 0.f;     // per lane, this row
+  float ent = 0.f, n_sparse = 0.f, n_allowed = 0.f;  // per lane, this row (ent: sum w log2 w)
   float t_n = 0.f, t_s = 0.f, t_l = 0.f, t_ss = 0.f, t_ll = 0.f, t_sl = 0.f;  // tau sums
 
   load_tile(0);
@@ -1097,30 +1097,40 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128),
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 16 * (r >> 3) + 8 * half + (r & 7);
         const bool ok = !((p.causal && key > my_q) || key >= p.Tk) && my_q < p.Tq;
-        if (!ok) continue;
         const float sd = sacc[r];          // q.k
         const float s = sd * scale;        // the scaled score
+        // log2 phi, phi = softplus(s) + 1e-6 as the forward's s^tau map forms
+        // it: max(s, 0) + log1p(e^-|s|) with the rounding of 1 + e corrected
+        const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+        const float u1 = 1.f + e;
+        const float c = (u1 - 1.f) - e;
+        const float lp = __builtin_amdgcn_logf(
+            fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c) + 1e-6f);
         float wgt;
         if (is_yat(VAR)) {
           const float nkr = r < 4 ? n0[r] : r < 8 ? n1[r - 4] : r < 12 ? n2[r - 8] : n3[r - 12];
           const float d2 = fmaf(-2.f, sd, nq + nkr);
           const float u = sd + bias;
-          wgt = yat_numerator<VAR>(u, p.yat_power) / (fmaxf(d2, 0.f) + eps) * inv_mass;
+          wgt = yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps) *
+                inv_mass;
         } else if (VAR == kSoftmax) {
-          wgt = exp2f(fmaf(sd, scale * kLog2e, -xmax)) * inv_mass;
+          wgt = __builtin_amdgcn_exp2f(fmaf(sd, scale * kLog2e, -xmax)) * inv_mass;
         } else {
-          wgt = powf(softplus_precise(s) + 1e-6f, tau) * inv_mass;
+          wgt = __builtin_amdgcn_exp2f(tau * lp) * inv_mass;
         }
-        if (wgt > 0.f) ent += wgt * logf(wgt);
-        n_sparse += wgt < p.sparsity_threshold ? 1.f : 0.f;
-        n_allowed += 1.f;
-        const float L = logf(softplus_precise(s) + 1e-6f);
-        t_n += 1.f;
-        t_s += s;
+        wgt = ok ? wgt : 0.f;
+        // w log2 w (weights below the smallest normal float add nothing)
+        ent += wgt >= 1.17549435e-38f ? wgt * __builtin_amdgcn_logf(wgt) : 0.f;
+        n_sparse += ok && wgt < p.sparsity_threshold ? 1.f : 0.f;
+        n_allowed += ok ? 1.f : 0.f;
+        const float L = ok ? lp * kLn2 : 0.f;  // ln phi
+        const float sm = ok ? s : 0.f;
+        t_n += ok ? 1.f : 0.f;
+        t_s += sm;
         t_l += L;
-        t_ss = fmaf(s, s, t_ss);
+        t_ss = fmaf(sm, sm, t_ss);
         t_ll = fmaf(L, L, t_ll);
-        t_sl = fmaf(s, L, t_sl);
+        t_sl = fmaf(sm, L, t_sl);
       }
     }
     if (t + 1 < n_tiles) {
@@ -1136,7 +1146,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128),
   n_allowed = pair_sum(n_allowed);
   if (my_q < p.Tq && half == 0) {
     const int64_t r = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
-    if (p.row_entropy) p.row_entropy[r] = n_allowed > 1.f ? -ent / logf(n_allowed) : 0.f;
+    if (p.row_entropy)
+      p.row_entropy[r] = n_allowed > 1.f ? -ent * kLn2 / logf(n_allowed) : 0.f;  // ent in log2
     if (p.row_sparsity) p.row_sparsity[r] = n_sparse / n_allowed;
   }
   // tau sums of the workgroup: wave reduction, then the two waves in LDS
