@@ -42,6 +42,7 @@ def _units():
         units.append((f"attn_bf16_dk{dk}", "attn_bf16.hip", [f"-DSFS_DK={dk}"]))
         units.append((f"attn_bwd_dk{dk}", "attn_bwd.hip", [f"-DSFS_DK={dk}"]))
         units.append((f"attn_decode_dk{dk}", "attn_decode.hip", [f"-DSFS_DK={dk}"]))
+        units.append((f"attn_telemetry_dk{dk}", "attn_telemetry.hip", [f"-DSFS_DK={dk}"]))
     return units
 
 
