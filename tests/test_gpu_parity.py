@@ -230,6 +230,16 @@ def test_yat_tied_keys_with_tiny_eps(shape, rows):
     full_check(inp, "yat", True, "yat_tied_tiny_eps", block_rows=rows)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_head_grouped_dispatch(causal):
+    # 32 (batch, head) slices: the 256-row kernel hands each XCD its heads in
+    # groups of 4 (workgroup i -> XCD i % 8); every tile must still be computed
+    # exactly once, with GQA and a ragged last query tile
+    inp = make_custom(2, 16, 8, 600, 600, 64, 64, "bf16", causal, seed=27, qk_std=1.5)
+    for variant in ("yat", "softmax"):
+        full_check(inp, variant, causal, "head_grouped", block_rows=(256,))
+
+
 def test_kv_splits_more_chunks_than_tiles():
     # 64 chunks over 4 tiles of keys: most chunks are empty and write neutral partials
     inp = make_custom(1, 2, 2, 40, 100, 64, 64, "bf16", False, seed=21)
