@@ -158,26 +158,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   const int grp = w >> 2, gtid = tid & (GT - 1);
   const int col = lane & 31, half = lane >> 5;
 
-  // Workgroup -> (query tile, batch, head).  Workgroup i runs on XCD i % 8,
-  // and each XCD has its own L2.  When the heads divide evenly, each XCD takes
-  // its heads in groups of kHeadGroup and runs a group's query tiles together,
-  // heads fastest: the resident workgroups of an XCD then share 4 heads' K/V
-  // in its L2 instead of 8 (long_yat: 476 -> 284 MB fetched per launch).
-  // Otherwise heads vary fastest over the whole grid.  With a causal mask the
+  // Workgroup -> (query tile, batch, head) in XCD-aware head groups (the
+  // resident workgroups of an XCD share 4 heads' K/V in its L2 instead of 8:
+  // long_yat 476 -> 284 MB fetched per launch).  With a causal mask the
   // longest query tiles of a group go first.
-  constexpr int kXcds = 8, kHeadGroup = 4;
   const int n_qt = (p.Tq + BM - 1) / BM;
   const int nbh = p.B * p.Hq;
   int qt, bh;
-  if (nbh % (kXcds * kHeadGroup) == 0) {
-    const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
-    const int gi = l / (kHeadGroup * n_qt), r = l - gi * (kHeadGroup * n_qt);
-    qt = r / kHeadGroup;
-    bh = x + kXcds * (gi * kHeadGroup + r - qt * kHeadGroup);
-  } else {
-    qt = blockIdx.x / nbh;
-    bh = blockIdx.x - qt * nbh;
-  }
+  grid_tile_slice(blockIdx.x, n_qt, nbh, qt, bh);
   if (p.causal) qt = n_qt - 1 - qt;
   const int b = bh / p.Hq, h = bh - b * p.Hq;
   const int hk = h / (p.Hq / p.Hkv);

@@ -269,7 +269,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   const bool is_a = w < NP;
   const int pr = w & (NP - 1);
   // Workgroup -> (key tile, batch, kv head), heads fastest.  With a causal
-  // mask the first key tiles have the most queries and go first.
+  // mask the first key tiles have the most queries and go first.  (Grouping
+  // heads per XCD as the forward does measured 1 % slower here.)
   const int nbh = p.B * p.Hkv;
   const int kt = blockIdx.x / nbh;
   const int bh = blockIdx.x - kt * nbh;

@@ -36,6 +36,24 @@ __host__ __device__ inline int64_t nk_pitch(int64_t Tk) { return (Tk + 63) / 64 
 // are cut into this many chunks of whole tiles (small-grid kernels only);
 // each chunk writes unnormalised partials that a combine kernel merges.
 constexpr int kDeviceCUs = 256;
+// Workgroup i of a grid of n_t tiles x n_s slices ((batch, head) pairs) runs
+// on XCD i % kXcds, and each XCD has its own L2.  When the slices divide
+// evenly, each XCD takes its slices in groups of kSliceGroup and runs a
+// group's tiles together, slices fastest, so that its resident workgroups
+// share a few slices' operands in L2; otherwise slices vary fastest over the
+// whole grid.  t is the tile in dispatch order (0 first), s the slice.
+constexpr int kXcds = 8, kSliceGroup = 4;
+__device__ __forceinline__ void grid_tile_slice(int i, int n_t, int n_s, int& t, int& s) {
+  if (n_s % (kXcds * kSliceGroup) == 0) {
+    const int x = i % kXcds, l = i / kXcds;
+    const int gi = l / (kSliceGroup * n_t), r = l - gi * (kSliceGroup * n_t);
+    t = r / kSliceGroup;
+    s = x + kXcds * (gi * kSliceGroup + r - t * kSliceGroup);
+  } else {
+    t = i / n_s;
+    s = i - t * n_s;
+  }
+}
 constexpr int kMaxKvSplits = 64;
 // rows = kDecodeRows: the vector kernel for at most this many query rows per
 // key/value head (the g heads of a group x T_q packed together), one
