@@ -214,6 +214,24 @@ def test_decode_kernel_tied_and_yat_options():
         full_check(inp, "yat", False, "decode_yat_opts", block_rows=(8,), yat_opts=opts)
 
 
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+def test_decode_kernel_strided_gqa_determinism(variant):
+    """The decode kernel's arithmetic per row does not depend on how rows are
+    packed or on the storage strides: [B, T, H, d] storage, K/V repeated to one
+    query row per key/value head, and a second call all give identical bits."""
+    inp = make_custom(2, 8, 2, 1, 1000, 128, 128, "bf16", False, seed=28)
+    q, k, v, prm = to_device(inp)
+    a = run_gpu(q, k, v, prm, variant, False, block_rows=8)
+    qs, ks, vs = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    assert ks.stride(2) == 2 * 128
+    b = run_gpu(qs, ks, vs, prm, variant, False, block_rows=8)
+    c = run_gpu(q, k.repeat_interleave(4, dim=1).contiguous(),
+                v.repeat_interleave(4, dim=1).contiguous(), prm, variant, False, block_rows=8)
+    d = run_gpu(q, k, v, prm, variant, False, block_rows=8)
+    for x, y, z, u in zip(a, b, c, d):
+        assert torch.equal(x, y) and torch.equal(x, z) and torch.equal(x, u)
+
+
 @pytest.mark.parametrize("shape,rows", [
     ((2, 4, 4, 200, 200, 128, 128), BLOCK_ROWS),     # every tile kernel
     ((1, 2, 2, 100, 100, 64, 32), BLOCK_ROWS),
