@@ -40,7 +40,7 @@ mass and max_score per branch) are those stated in ``attn_oracle.c``.
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` (worked examples printed on the pages, closed
 forms, invariants and brute force).  The mass and max_score conventions for
-softmax and s^tau and the GQA mapping are conventions of this build, pinned
+softmax and s^tau and the GQA mapping are conventions chosen here, pinned
 only by brute force and self-consistency (parity unpinned by the pages).
 ``attn_bwd_np`` is pinned in ``tests/test_oracle_bwd_pins.py`` to central
 finite differences of the C forward, to PyTorch autograd through its own
