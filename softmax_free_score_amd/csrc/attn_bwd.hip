@@ -72,6 +72,12 @@ namespace {
 
 __device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+// acc + the two bf16 halves of x, in fp32, one instruction (v_dot2 with ones)
+__device__ __forceinline__ float add_bf16_pair(unsigned x, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, acc, false);
+}
 
 // A-operand fragment of v_mfma_f32_32x32x16_bf16 whose matrix is the
 // transpose of a row-major LDS tile R (32 rows, pitch `ld` elements, row j
@@ -401,7 +407,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   f32x16 acc[AB];
 #pragma unroll
   for (int i = 0; i < AB; ++i) acc[i] = f32x16{};
-  float corr = 0.f;  // B, Yat: sum over the lane's queries of B'/2 = bf16(g/2) - A/2
+  // B, Yat: sums over the lane's queries of bf16(g/2) and of A/2; their
+  // difference is the sum of B'/2 = bf16(g/2) - A/2
+  float corr = 0.f, asum = 0.f;
   HeadC hc{};        // A: constants of query head hk g + hc_gi, the head last mapped
   int hc_gi = -1;
 
@@ -497,8 +505,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
           v[o] = grad_from_mult<VAR>(mult[r], pacc[r], D, Z, av[o]);
         }
         pk[s][e2] = pack_bf16(v[0], v[1]);
-        if (is_yat(VAR))
-          corr += (bf16_lo(pk[s][e2]) - av[0]) + (bf16_hi(pk[s][e2]) - av[1]);
+        if (is_yat(VAR)) {
+          corr = add_bf16_pair(pk[s][e2], corr);
+          asum += av[0] + av[1];
+        }
       }
     }
 #pragma unroll
@@ -595,7 +605,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
     }
   }
   if (!is_a) {
-    if (is_yat(VAR)) corr = 2.f * pair_sum(corr);  // the kernel carries g/2 and A/2
+    if (is_yat(VAR)) corr = 2.f * pair_sum(corr - asum);  // the kernel carries g/2 and A/2
     if (my_k < p.Tk) {
       unsigned short* dkrow = (unsigned short*)p.dk_ + (int64_t)b * p.ks[0] +
                               (int64_t)hk * p.ks[1] + (int64_t)my_k * p.ks[2];
@@ -762,7 +772,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   f32x16 accQ[KB];
 #pragma unroll
   for (int i = 0; i < KB; ++i) accQ[i] = f32x16{};
-  float corr = 0.f;            // Yat: sum over the lane's keys of B'/2 = bf16(g/2) - A/2
+  float corr = 0.f;            // Yat: sum over the lane's keys of bf16(g/2) (minus sum0 below:
+                               // the sum of B'/2 = bf16(g/2) - A/2)
   float sum0 = 0.f, sum1 = 0.f;  // Yat: sum A/2, sum B/2; s^tau: sum w (dp - D) log2(phi)
   float dsum = 0.f;            // DELTA: sum over the lane's keys of w dp (Yat: kappa dp)
   float msum = 0.f;            // DELTA, Yat: sum over the lane's keys of kappa
@@ -813,7 +824,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
         pg[s][e2] = pack_bf16(gv[0], gv[1]);
         if (is_yat(VAR)) {
           // (g/2 and A/2: the sums are doubled where they are used)
-          corr += (bf16_lo(pg[s][e2]) - av[0]) + (bf16_hi(pg[s][e2]) - av[1]);
+          corr = add_bf16_pair(pg[s][e2], corr);
           sum0 += av[0] + av[1];
           sum1 += (gv[0] - av[0]) + (gv[1] - av[1]);
         } else if (VAR == kStau) {
@@ -874,7 +885,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
     return;
   }
 
-  if (is_yat(VAR)) corr = 2.f * pair_sum(corr);  // the kernel carries g/2 and A/2
+  if (is_yat(VAR)) corr = 2.f * pair_sum(corr - sum0);  // the kernel carries g/2 and A/2
   if (my_q < p.Tq) {
     unsigned short* dqrow = (unsigned short*)p.dq + (int64_t)b * p.qs[0] +
                             (int64_t)h * p.qs[1] + (int64_t)my_q * p.qs[2];
