@@ -149,10 +149,12 @@ __device__ __forceinline__ float pair_weight(float sd, float Z, float nqk, const
 
 // The gradient score of one pair from sd, dp = dout.v, the row's D and Z and
 // (Yat) nqk, before the 1/sqrt(d_k) of softmax and s^tau, plus the terms of
-// the Yat correction (a) and of the s^tau parameter sum (lt).
-//   Yat:   returns g/2 and a = A/2 (the kernels double the results; exact):
-//          with r = 1/den, u = q.k + b:  A/2 = (dp - D) Z u r,
-//          g/2 = A/2 + B/2 = A/2 (1 + u r)  since B/A = kappa/u = u r.
+// the Yat correction and parameter sums (a, lt) and of the s^tau parameter
+// sum (lt).
+//   Yat:   returns g/2, a = A/2 and lt = B/2 (the kernels double the
+//          results; exact): with r = 1/den, u = q.k + b:
+//          A/2 = (dp - D) Z u r, B/2 = A/2 u r, g/2 = A/2 + B/2
+//          (B/A = kappa/u = u r).
 //   softmax: g = w (dp - D);  s^tau: g = w (dp - D) tau sigmoid(s) / phi,
 //          lt = w (dp - D) log2(phi).
 template <int VAR>
@@ -161,9 +163,9 @@ __device__ __forceinline__ void pair_grad(float sd, float dp, float D, float Z, 
   if constexpr (is_yat(VAR)) {
     const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
     const float ur = (sd + hc.bias) * rden;
-    a = (dp - D) * Z * (sd + hc.bias) * rden;
-    g = fmaf(a, ur, a);
-    lt = 0.f;
+    a = (dp - D) * Z * ur;
+    lt = a * ur;
+    g = a + lt;
   } else if constexpr (VAR == kSoftmax) {
     g = __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z)) * (dp - D);
     a = lt = 0.f;
@@ -826,7 +828,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
           // (g/2 and A/2: the sums are doubled where they are used)
           corr = add_bf16_pair(pg[s][e2], corr);
           sum0 += av[0] + av[1];
-          sum1 += (gv[0] - av[0]) + (gv[1] - av[1]);
+          sum1 += lv[0] + lv[1];
         } else if (VAR == kStau) {
           sum0 += lv[0] + lv[1];
         }
