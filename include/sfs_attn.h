@@ -247,8 +247,8 @@ int attn_telemetry(const attn_desc* desc, const void* q, const void* k, int vari
  * deps_raw       d L / d eps_raw); dlog_tau [Hq] for ATTN_STAU.  NULL means
  * dlog_tau       "not computed"; ignored for the other maps.
  * workspace      attn_bwd_workspace_bytes(desc, variant) bytes, 16-byte
- *                aligned: Yat |q|^2 and |k|^2 rows, per-row D and Z, and
- *                per-workgroup parameter sums.
+ *                aligned: Yat |q|^2 + b and |k|^2 + b rows per query head,
+ *                per-row D and Z, and per-workgroup parameter sums.
  * desc->block_rows and desc->kv_splits are forward launch options and are
  * not used here.  Ownership, asynchrony, errors and empty problems as
  * attn_fwd; ATTN_ERR_UNSUPPORTED for fp32 storage.  The standard maps only

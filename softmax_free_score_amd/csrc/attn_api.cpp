@@ -373,7 +373,7 @@ BwdWs bwd_ws(const attn_desc* d, int variant) {
   const size_t n_qt = (size_t)((d->Tq + sfs::kBwdQRows - 1) / sfs::kBwdQRows);
   size_t off = 0;
   w.nk = off;
-  if (variant == ATTN_YAT) off += align256((size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4);
+  if (variant == ATTN_YAT) off += align256((size_t)(d->B * d->Hq * sfs::nk_pitch(d->Tk)) * 4);
   w.nq = off;
   if (variant == ATTN_YAT) off += align256(rows_q);
   w.rd = off;

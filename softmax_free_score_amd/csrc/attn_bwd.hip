@@ -125,14 +125,15 @@ __device__ __forceinline__ HeadC head_consts(const BwdProblem& p, int h) {
   return c;
 }
 
-// The forward's weight of one pair from sd = q.k, the row normaliser Z
-// (softmax: L, the log2 normaliser) and, for Yat, nqk = |q|^2 + |k|^2.
+// The forward's weight of one pair from the score sd, the row normaliser Z
+// (softmax: L, the log2 normaliser) and, for Yat, nqk.  Yat's score chains
+// start at b, as the forward's do: sd = u = q.k + b and nqk = (|q|^2 + b) +
+// (|k|^2 + b), so d2 = nqk - 2u; for softmax and s^tau sd = q.k.
 template <int VAR>
 __device__ __forceinline__ float pair_weight(float sd, float Z, float nqk, const HeadC& hc) {
   if constexpr (is_yat(VAR)) {
     const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
-    const float u = sd + hc.bias;
-    return u * (u * rden) * Z;
+    return sd * (sd * rden) * Z;
   } else if constexpr (VAR == kSoftmax) {
     return __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
   } else {
@@ -162,7 +163,7 @@ __device__ __forceinline__ void pair_grad(float sd, float dp, float D, float Z, 
                                           const HeadC& hc, float& g, float& a, float& lt) {
   if constexpr (is_yat(VAR)) {
     const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
-    const float ur = (sd + hc.bias) * rden;
+    const float ur = sd * rden;
     a = (dp - D) * Z * ur;
     lt = a * ur;
     g = a + lt;
@@ -197,10 +198,9 @@ __device__ __forceinline__ float pair_weight_mult(float sd, float Z, float nqk, 
                                                   float& mult) {
   if constexpr (is_yat(VAR)) {
     const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
-    const float u = sd + hc.bias;
-    const float ur = u * rden;
+    const float ur = sd * rden;
     mult = ur;
-    return u * ur * Z;
+    return sd * ur * Z;
   } else if constexpr (VAR == kSoftmax) {
     const float w = __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
     mult = w;
@@ -314,9 +314,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   const int per_head = n_qt - qt0;
   const int n_it = g * per_head;           // 0 when T_q == 0: only zeros are stored
   const int64_t qpitch = nk_pitch(p.Tq);
+  // A, Yat: |k|^2 + b of this lane's key for the head being mapped
   float nk = 0.f;
-  if (is_yat(VAR) && n_it > 0 && my_k < p.Tk)
-    nk = p.nk[((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) + my_k];
+  auto load_nk = [&](int gi) {
+    if (is_yat(VAR) && my_k < p.Tk)
+      nk = p.nk[((int64_t)b * p.Hq + hk * g + gi) * nk_pitch(p.Tk) + my_k];
+  };
 
   // Tile it covers query head hk * g + it / per_head, query tile
   // qt0 + it % per_head; the loops below step these instead of dividing.
@@ -420,6 +423,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   auto weights = [&](auto mask_tag, int slot, int ss, int qb, u32x4* pk) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 sacc = {};
+    if (is_yat(VAR)) {
+      // the chain starts at b (see pair_weight), from a scalar for every tile
+      int bb = __builtin_amdgcn_readfirstlane(__float_as_int(hc.bias));
+      asm volatile("" : "+s"(bb));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = __int_as_float(bb);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQ[slot][col * QLD + 16 * s + 8 * half]),
@@ -554,6 +564,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   if (n_it > 0 && is_a && active(cur.qt)) {
     hc = head_consts<VAR, DK>(p, hk * g + cur.gi);
     hc_gi = cur.gi;
+    load_nk(cur.gi);
     map_tile(cur, 0, 0, pk_cur);
   }
   __syncthreads();
@@ -573,6 +584,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
         if (nxt.gi != hc_gi) {
           hc = head_consts<VAR, DK>(p, hk * g + nxt.gi);
           hc_gi = nxt.gi;
+          load_nk(nxt.gi);
         }
         u32x4 pk_nxt[2];
         map_tile(nxt, (it + 1) % NS, (it + 1) & 1, pk_nxt);
@@ -720,7 +732,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   }
   const HeadC hc = head_consts<VAR, DK>(p, h);
   const float* nk_slice =
-      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hkv + hk) * nk_pitch(p.Tk) : nullptr;
+      is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;  // |k|^2 + b
+  const int b_bits = __builtin_amdgcn_readfirstlane(__float_as_int(hc.bias));
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
@@ -784,6 +797,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   auto scores = [&](auto mask_tag, int buf, int k0, u32x4* pg) {
     constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 sacc = {}, pacc = {};
+    if (is_yat(VAR)) {
+      // the score chain starts at b (see pair_weight), rebuilt from a scalar
+      // for every tile rather than held in 16 registers
+      int bb = b_bits;
+      asm volatile("" : "+s"(bb));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = __int_as_float(bb);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       sacc = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sK[buf][col * KLD + 16 * s + 8 * half]),
@@ -938,16 +959,44 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   }
 }
 
+// Yat: |x_j|^2 + b_h for every row of the key or query slice that query head
+// h reads (x head h / (Hq / Hx)), by the same MFMA sequence and start value b
+// as the score chains.  One wave per 32 rows; grid (ceil(T / 128), Hq, B),
+// 256 threads; output [B][Hq][nk_pitch(T)].
+template <int DK>
+__global__ __launch_bounds__(256) void norms_plus_bias_bf16(const unsigned short* x, int64_t s0,
+                                                            int64_t s1, int64_t s2, int Hx,
+                                                            int T, int Hq, const float* b_raw,
+                                                            float* out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y, hx = h / (Hq / Hx);
+  const int row = blockIdx.x * 128 + 32 * w + col;
+  const unsigned short* base = x + (int64_t)b * s0 + (int64_t)hx * s1;
+  const uint32_t bytes = slice_bytes(T, s2, DK);
+  const rsrc_t r = make_rsrc(base, bytes);
+  const uint32_t off = row < T ? (uint32_t)(((int64_t)row * s2 + 8 * half) * 2) : bytes;
+  const float bias = softplus_precise(b_raw[h]);  // as head_consts forms it
+  f32x16 g;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) g[i] = bias;
+#pragma unroll
+  for (int s = 0; s < DK / 16; ++s)
+    g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
+               __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
+  if (row < T && holds_diag(col, half)) out[((int64_t)b * Hq + h) * nk_pitch(T) + row] = diag_of(g, col);
+}
+
 template <int VAR, int DV>
 hipError_t launch_bwd_variant(const BwdProblem& p, hipStream_t stream) {
   constexpr int DK = SFS_DK;
   if (is_yat(VAR) && p.Tq > 0) {
-    hipLaunchKernelGGL(row_norms_bf16<DK>, dim3((p.Tk + 127) / 128, p.Hkv, p.B), dim3(256), 0,
-                       stream, (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv, p.Tk,
-                       p.nk);
-    hipLaunchKernelGGL(row_norms_bf16<DK>, dim3((p.Tq + 127) / 128, p.Hq, p.B), dim3(256), 0,
-                       stream, (const unsigned short*)p.q, p.qs[0], p.qs[1], p.qs[2], p.Hq, p.Tq,
-                       p.nq);
+    hipLaunchKernelGGL(norms_plus_bias_bf16<DK>, dim3((p.Tk + 127) / 128, p.Hq, p.B), dim3(256),
+                       0, stream, (const unsigned short*)p.k, p.ks[0], p.ks[1], p.ks[2], p.Hkv,
+                       p.Tk, p.Hq, p.b_raw, p.nk);
+    hipLaunchKernelGGL(norms_plus_bias_bf16<DK>, dim3((p.Tq + 127) / 128, p.Hq, p.B), dim3(256),
+                       0, stream, (const unsigned short*)p.q, p.qs[0], p.qs[1], p.qs[2], p.Hq,
+                       p.Tq, p.Hq, p.b_raw, p.nq);
   }
   const unsigned n_q = (unsigned)((p.Tq + kBwdQRows - 1) / kBwdQRows) * (unsigned)p.B *
                        (unsigned)p.Hq;

@@ -190,8 +190,8 @@ struct BwdProblem {
   int variant;
   int causal;
   // workspace
-  float* nq;         // Yat: |q_i|^2 [B*Hq][nk_pitch(Tq)]
-  float* nk;         // Yat: |k_j|^2 [B*Hkv][nk_pitch(Tk)]
+  float* nq;         // Yat: |q_i|^2 + b_h [B*Hq][nk_pitch(Tq)]
+  float* nk;         // Yat: |k_j|^2 + b_h per query head h [B*Hq][nk_pitch(Tk)]
   float* row_d;      // D_i = sum_j w_ij dp_ij [B*Hq][nk_pitch(Tq)] (0 past T_q)
   float* row_z;      // row normaliser [B*Hq][nk_pitch(Tq)] (0 past T_q)
   double* prm_part;  // [Hq][B][n_qt][2] per-workgroup sums for the parameter

@@ -277,7 +277,7 @@ def test_bwd_workspace_bytes():
     ws = lambda v: lib.attn_bwd_workspace_bytes(ctypes.byref(d), v)
     assert ws(attn.ATTN_SOFTMAX) == 2 * al(rows)
     assert ws(attn.ATTN_STAU) == 2 * al(rows) + prm
-    nk = 2 * 2 * 128 * 4
+    nk = 2 * 4 * 128 * 4                                      # |k|^2 + b per query head
     assert ws(attn.ATTN_YAT) == al(nk) + 3 * al(rows) + prm
     assert ws(7) == 0
     d.dtype = attn.ATTN_F32
