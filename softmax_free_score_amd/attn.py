@@ -110,7 +110,8 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def make_desc(q, k, v, out=None, block_rows=0, kv_splits=0) -> AttnDesc:
     """Descriptor from 4-D tensors (strides in elements, last axis contiguous).
-    ``block_rows`` 0 lets the library pick the bf16 kernel; 64/128/256 force one.
+    ``block_rows`` 0 lets the library pick the bf16 kernel; 64/128/256 force a
+    tile kernel, 8 the decode kernel (at most 8 query rows per key/value head).
     ``kv_splits`` 0 lets the library decide whether to split the keys; 1 never;
     n >= 2 forces n chunks."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
