@@ -191,6 +191,7 @@ DECODE_FORCED = [
     (1, 2, 2, 3, 3, 32, 32, True),          # causal, fewer keys than a chunk
     (2, 2, 1, 4, 4, 128, 128, True),        # causal, 8 packed rows
     (1, 2, 1, 1, 17000, 64, 64, False),     # 67 chunks: the merge reads more than 64
+    (1, 2, 1, 1, 70001, 64, 32, False),     # 274 chunks, ragged last one
     (2, 3, 3, 1, 513, 32, 32, False),       # one row per kv head, ragged last chunk
 ]
 
