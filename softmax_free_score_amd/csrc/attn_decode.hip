@@ -40,6 +40,10 @@ namespace {
 
 constexpr int kChunk = 256;  // keys per workgroup
 
+// Key and value rows are read once per call: streaming (non-temporal) loads.
+__device__ __forceinline__ u32x4 ld128_stream(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
+}
 __device__ __forceinline__ float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
 #pragma unroll
   for (int t = 0; t < KIT; ++t) {
     const int j = j0 + 64 * w + KPI * t + kk;
-    kr[t] = ld128(rk, j < p.Tk ? (uint32_t)(((int64_t)j * p.ks[2] + 8 * cb) * 2) : k_bytes);
+    kr[t] = ld128_stream(rk, j < p.Tk ? (uint32_t)(((int64_t)j * p.ks[2] + 8 * cb) * 2) : k_bytes);
   }
   __syncthreads();
   if (w == 0) {
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
 #pragma unroll
   for (int t = 0; t < VIT; ++t) {
     const int j = j0 + 64 * w + VPI * t + vk;
-    vr[t] = ld128(rv, j < p.Tk ? (uint32_t)(((int64_t)j * p.vs[2] + 8 * vc) * 2) : v_bytes);
+    vr[t] = ld128_stream(rv, j < p.Tk ? (uint32_t)(((int64_t)j * p.vs[2] + 8 * vc) * 2) : v_bytes);
   }
 
   // Phase 2: row maxima and masses over the chunk (waves in order).
