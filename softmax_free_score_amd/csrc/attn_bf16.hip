@@ -378,10 +378,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   auto weights = [&](auto mask_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = t * BN;
-    auto allowed = [&](int kb, int r) {
-      const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-      return !((p.causal && key > my_q) || key >= p.Tk);
-    };
+    // key k0 + 8 half + o is allowed iff o <= lim (o: the element's offset,
+    // a compile-time constant), so the mask is one compare per element
+    const int lim = (p.causal ? min(my_q, p.Tk - 1) : p.Tk - 1) - (k0 + 8 * half);
+    auto allowed = [&](int kb, int r) { return kb * 32 + 16 * (r >> 3) + (r & 7) <= lim; };
     if (VAR == kSoftmax) {
       float tmax = -INFINITY;
 #pragma unroll
@@ -445,7 +445,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
             float kap = yat_numerator<VAR>(u, p.yat_power) * rc[r];
             if (MASK) kap = allowed(kb, r0 + r) ? kap : 0.f;
             sacc[kb][r0 + r] = kap;
-            mass += kap;
             mx = fmaxf(mx, kap);
           }
         }
@@ -483,6 +482,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
+        // Yat's mass is the sum of the bf16 weights the value MFMA takes
+        if (is_yat(VAR)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass);
+        }
         pb[kb][s] = __builtin_bit_cast(bf16x8, pw);
       }
   };
@@ -764,10 +768,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         sacc[kb] = mfma32(a, qf[s], sacc[kb]);
       }
 
-    auto allowed = [&](int kb, int r) {
-      const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-      return !((p.causal && key > my_q) || key >= p.Tk);
-    };
+    // key k0 + 8 half + o is allowed iff o <= lim (o: the element's offset,
+    // a compile-time constant), so the mask is one compare per element
+    const int lim = (p.causal ? min(my_q, p.Tk - 1) : p.Tk - 1) - (k0 + 8 * half);
+    auto allowed = [&](int kb, int r) { return kb * 32 + 16 * (r >> 3) + (r & 7) <= lim; };
 
     if (VAR == kSoftmax) {
       float tmax = -INFINITY;
@@ -825,7 +829,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           float kap = yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
           if (MASK) kap = allowed(kb, r) ? kap : 0.f;
           sacc[kb][r] = kap;
-          mass += kap;
           mx = fmaxf(mx, kap);
         }
       }
@@ -864,6 +867,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
+        // Yat's mass is the sum of the bf16 weights the value MFMA takes
+        if (is_yat(VAR)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass);
+        }
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
         for (int d = 0; d < DB; ++d) {

@@ -72,12 +72,6 @@ namespace {
 
 __device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
-// acc + the two bf16 halves of x, in fp32, one instruction (v_dot2 with ones)
-__device__ __forceinline__ float add_bf16_pair(unsigned x, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, acc, false);
-}
 
 // A-operand fragment of v_mfma_f32_32x32x16_bf16 whose matrix is the
 // transpose of a row-major LDS tile R (32 rows, pitch `ld` elements, row j

@@ -18,7 +18,7 @@ namespace {
 //
 // With the forward's row normaliser (mass, and max_score for softmax) the
 // weights of every allowed pair are recomputed exactly as the forward defines
-// them, and per row the pass accumulates sum w log2 w, the count of weights
+// them (Yat: kappa rounded to bf16, as the tile kernels weight the values), and per row the pass accumulates sum w log2 w, the count of weights
 // below the threshold and the count of allowed keys; per (head, batch, query
 // tile) it accumulates the sums that give tau* = Cov(s, ln phi(s)) /
 // Var(ln phi(s)) with s = q.k / sqrt(d_k), phi = softplus(s) + 1e-6 (the s^tau
@@ -168,8 +168,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128),
           const float nkr = r < 4 ? n0[r] : r < 8 ? n1[r - 4] : r < 12 ? n2[r - 8] : n3[r - 12];
           const float d2 = fmaf(-2.f, sd, nq + nkr);
           const float u = sd + bias;
-          wgt = yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps) *
-                inv_mass;
+          // the tile kernels' value MFMA takes kappa in bf16, and their mass sums those
+          const float kap =
+              yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
+          wgt = (float)(__bf16)kap * inv_mass;
         } else if (VAR == kSoftmax) {
           wgt = __builtin_amdgcn_exp2f(fmaf(sd, scale * kLog2e, -xmax)) * inv_mass;
         } else {

@@ -38,6 +38,11 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(unsigned, v);
 }
+// acc + the two bf16 halves of x, in fp32, one instruction (v_dot2 with ones)
+__device__ __forceinline__ float add_bf16_pair(unsigned x, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), ones, acc, false);
+}
 // Two bf16 words from two packed pairs, one byte permute each: the low
 // halves of a and b (a's in the low half of the result), or the high halves.
 __device__ __forceinline__ unsigned lo_halves(unsigned a, unsigned b) {
