@@ -39,6 +39,8 @@
 //     same MFMA instruction, k-step order and start value as the score tile
 //     (diagonals of X X^T), so for a key equal to its query the three terms
 //     cancel to exactly 0 and the peak (|q|^2 + b)^2 / eps is reproduced.
+//     Both row terms are held scaled by 2^-96, which lets the clamp at 0 and
+//     the + eps ride on two FMAs (yat_den).
 //   * Yat and s^tau accumulate sum(p v) and the mass in one pass with no
 //     running maximum; softmax keeps a reference maximum that moves only when
 //     a tile's maximum exceeds it by more than 2^8 (then O and the sum are
@@ -88,7 +90,21 @@ __device__ __forceinline__ float yat_bias(const Problem& p, int h) {
   return p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
 }
 
-// Yat pre-pass: |k_j|^2 + b_h for every key row and query head, by the same
+// Yat's denominator max(d2, 0) + eps in three instructions.  The row terms
+// |q|^2 + b and |k|^2 + b are kept scaled by 2^-96 (exact: a power of two), so
+// y = 2^-96 d2 comes from one FMA whose result the clamp modifier limits to
+// [0, 1], and y 2^96 + eps is one more FMA with a single rounding: the same
+// value as max(d2, 0) + eps computed unscaled, ties (d2 = 0) included.  Limits:
+// d2 is capped at 2^96, and d2 below 2^-30 loses bits (denormal y); neither
+// changes the denominator unless eps is below ~1e-15 or |q|^2 + |k|^2 exceeds
+// the range where (q.k + b)^2 is finite.
+constexpr float kNormScale = 0x1p-96f;
+__device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps) {
+  const float y = __builtin_amdgcn_fmed3f(fmaf(u, -2.f * kNormScale, nqk_scaled), 0.f, 1.f);
+  return fmaf(y, 0x1p96f, eps);
+}
+
+// Yat pre-pass: (|k_j|^2 + b_h) 2^-96 for every key row and query head, by the same
 // MFMA sequence and start value as the score tile (see score_init).  One wave
 // per 32 rows; grid (ceil(T_k / 128), Hq, B), 256 threads; output
 // [B][Hq][nk_pitch(T_k)].
@@ -109,7 +125,7 @@ __global__ __launch_bounds__(256) void yat_key_norms_bf16(Problem p) {
     g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
                __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
   if (row < p.Tk && holds_diag(col, half))
-    p.nk[((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) + row] = diag_of(g, col);
+    p.nk[((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) + row] = diag_of(g, col) * kNormScale;
 }
 
 // Fused forward, "ping-pong" schedule.
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
     f32x16 g = sinit;
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
-    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
+    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
   }
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
@@ -436,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           float den[8], rc[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r)
-            den[r] = fmaxf(fmaf(-2.f, sacc[kb][r0 + r], nq + nk[r0 + r]), 0.f) + eps;
+            den[r] = yat_den(sacc[kb][r0 + r], nq + nk[r0 + r], eps);
 #pragma unroll
           for (int r = 0; r < 8; ++r) rc[r] = __builtin_amdgcn_rcpf(den[r]);
 #pragma unroll
@@ -650,7 +666,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     f32x16 g = sinit;
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
-    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col);
+    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
   }
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
@@ -825,8 +841,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float u = sacc[kb][r];  // q.k + b
-          const float d2 = fmaf(-2.f, u, nq + nk[r]);
-          float kap = yat_numerator<VAR>(u, p.yat_power) * __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + eps);
+          float kap = yat_numerator<VAR>(u, p.yat_power) *
+                      __builtin_amdgcn_rcpf(yat_den(u, nq + nk[r], eps));
           if (MASK) kap = allowed(kb, r) ? kap : 0.f;
           sacc[kb][r] = kap;
           mx = fmaxf(mx, kap);
