@@ -90,20 +90,6 @@ __device__ __forceinline__ float yat_bias(const Problem& p, int h) {
   return p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
 }
 
-// Yat's denominator max(d2, 0) + eps in three instructions.  The row terms
-// |q|^2 + b and |k|^2 + b are kept scaled by 2^-96 (exact: a power of two), so
-// y = 2^-96 d2 comes from one FMA whose result the clamp modifier limits to
-// [0, 1], and y 2^96 + eps is one more FMA with a single rounding: the same
-// value as max(d2, 0) + eps computed unscaled, ties (d2 = 0) included.  Limits:
-// d2 is capped at 2^96, and d2 below 2^-30 loses bits (denormal y); neither
-// changes the denominator unless eps is below ~1e-15 or |q|^2 + |k|^2 exceeds
-// the range where (q.k + b)^2 is finite.
-constexpr float kNormScale = 0x1p-96f;
-__device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps) {
-  const float y = __builtin_amdgcn_fmed3f(fmaf(u, -2.f * kNormScale, nqk_scaled), 0.f, 1.f);
-  return fmaf(y, 0x1p96f, eps);
-}
-
 // Yat pre-pass: (|k_j|^2 + b_h) 2^-96 for every key row and query head, by the same
 // MFMA sequence and start value as the score tile (see score_init).  One wave
 // per 32 rows; grid (ceil(T_k / 128), Hq, B), 256 threads; output

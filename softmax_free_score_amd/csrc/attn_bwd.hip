@@ -121,12 +121,12 @@ __device__ __forceinline__ HeadC head_consts(const BwdProblem& p, int h) {
 
 // The forward's weight of one pair from the score sd, the row normaliser Z
 // (softmax: L, the log2 normaliser) and, for Yat, nqk.  Yat's score chains
-// start at b, as the forward's do: sd = u = q.k + b and nqk = (|q|^2 + b) +
-// (|k|^2 + b), so d2 = nqk - 2u; for softmax and s^tau sd = q.k.
+// start at b, as the forward's do: sd = u = q.k + b and nqk = ((|q|^2 + b) +
+// (|k|^2 + b)) 2^-96, so d2 = 2^96 nqk - 2u; for softmax and s^tau sd = q.k.
 template <int VAR>
 __device__ __forceinline__ float pair_weight(float sd, float Z, float nqk, const HeadC& hc) {
   if constexpr (is_yat(VAR)) {
-    const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
+    const float rden = __builtin_amdgcn_rcpf(yat_den(sd, nqk, hc.eps));
     return sd * (sd * rden) * Z;
   } else if constexpr (VAR == kSoftmax) {
     return __builtin_amdgcn_exp2f(fmaf(sd, hc.c_sm, -Z));
@@ -156,7 +156,7 @@ template <int VAR>
 __device__ __forceinline__ void pair_grad(float sd, float dp, float D, float Z, float nqk,
                                           const HeadC& hc, float& g, float& a, float& lt) {
   if constexpr (is_yat(VAR)) {
-    const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
+    const float rden = __builtin_amdgcn_rcpf(yat_den(sd, nqk, hc.eps));
     const float ur = sd * rden;
     a = (dp - D) * Z * ur;
     lt = a * ur;
@@ -191,7 +191,7 @@ template <int VAR>
 __device__ __forceinline__ float pair_weight_mult(float sd, float Z, float nqk, const HeadC& hc,
                                                   float& mult) {
   if constexpr (is_yat(VAR)) {
-    const float rden = __builtin_amdgcn_rcpf(fmaxf(fmaf(-2.f, sd, nqk), 0.f) + hc.eps);
+    const float rden = __builtin_amdgcn_rcpf(yat_den(sd, nqk, hc.eps));
     const float ur = sd * rden;
     mult = ur;
     return sd * ur * Z;
@@ -953,10 +953,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   }
 }
 
-// Yat: |x_j|^2 + b_h for every row of the key or query slice that query head
-// h reads (x head h / (Hq / Hx)), by the same MFMA sequence and start value b
-// as the score chains.  One wave per 32 rows; grid (ceil(T / 128), Hq, B),
-// 256 threads; output [B][Hq][nk_pitch(T)].
+// Yat: (|x_j|^2 + b_h) 2^-96 for every row of the key or query slice that
+// query head h reads (x head h / (Hq / Hx)), by the same MFMA sequence and
+// start value b as the score chains (the scaling is the one yat_den takes).
+// One wave per 32 rows; grid (ceil(T / 128), Hq, B), 256 threads; output
+// [B][Hq][nk_pitch(T)].
 template <int DK>
 __global__ __launch_bounds__(256) void norms_plus_bias_bf16(const unsigned short* x, int64_t s0,
                                                             int64_t s1, int64_t s2, int Hx,
@@ -978,7 +979,8 @@ __global__ __launch_bounds__(256) void norms_plus_bias_bf16(const unsigned short
   for (int s = 0; s < DK / 16; ++s)
     g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
                __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
-  if (row < T && holds_diag(col, half)) out[((int64_t)b * Hq + h) * nk_pitch(T) + row] = diag_of(g, col);
+  if (row < T && holds_diag(col, half))
+    out[((int64_t)b * Hq + h) * nk_pitch(T) + row] = diag_of(g, col) * kNormScale;
 }
 
 template <int VAR, int DV>
