@@ -23,9 +23,9 @@
 // merges them.  Maps as in attn_bf16.hip ("Softmax-Free Attention in JAX/Flax
 // NNX", "One module, two compatibility functions"; "NNX Scaled Dot-Product
 // Attention", displayed equation; the "s^tau" forum post, core formula).
-// |q|^2, |k|^2 and q.k are formed by the same per-lane FMA order and the same
-// shuffle tree, so for a key equal to its query d2 = |q|^2 + |k|^2 - 2 q.k is
-// exactly 0.
+// |q|^2, |k|^2 and q.k are formed by the same per-lane v_dot2 order on the
+// bf16 pairs and the same shuffle tree, so for a key equal to its query
+// d2 = |q|^2 + |k|^2 - 2 q.k is exactly 0.
 #include "bf16_common.h"
 
 #ifndef SFS_DK
@@ -64,11 +64,15 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
   return x;
 }
-// Partial dot product of 8 columns: a . b in column order.
-__device__ __forceinline__ float dot8(const float* a, const float* b) {
+// Partial dot product of 8 bf16 columns held as 4 packed pairs (column 2e in
+// the low half): one v_dot2_f32_bf16 per pair, pairs in column order, fp32
+// accumulation.
+__device__ __forceinline__ float dot8(const unsigned* a, const unsigned* b) {
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s = fmaf(a[e], b[e], s);
+  for (int e = 0; e < 4; ++e)
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[e]),
+                                        __builtin_bit_cast(bf16x2, b[e]), s, false);
   return s;
 }
 
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
   constexpr int VB = DV / 8;            // 8-column blocks of a value row
   constexpr int VPI = 64 / VB;
   constexpr int VIT = 64 / VPI;
-  __shared__ __attribute__((aligned(16))) float sQ[NR][DK];
+  __shared__ __attribute__((aligned(16))) unsigned sQ[NR][DK / 2];  // bf16 pairs
   __shared__ float sC[NR][4];           // |q|^2, b (Yat) / tau (s^tau), eps
   __shared__ float sP[NR][kChunk];      // weights of the chunk (softmax: exponent first)
   __shared__ float sRed[NW][NR][2];
@@ -99,13 +103,14 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
   const float scale = 1.0f / sqrtf((float)DK);
   const int kk = lane / CB, cb = lane % CB;  // key sub-row, column block (phase 1)
 
-  // Query rows into LDS as fp32; row r is query head hk g + r / T_q, row r % T_q.
-  for (int idx = tid; idx < R * DK; idx += NT) {
-    const int r = idx / DK, d = idx - r * DK;
+  // Query rows into LDS as bf16 pairs; row r is query head hk g + r / T_q,
+  // row r % T_q.
+  for (int idx = tid; idx < R * DK / 2; idx += NT) {
+    const int r = idx / (DK / 2), d = 2 * (idx - r * (DK / 2));
     const int h = hk * g + r / p.Tq, i = r - (r / p.Tq) * p.Tq;
     const unsigned short* qrow = (const unsigned short*)p.q + (int64_t)b * p.qs[0] +
                                  (int64_t)h * p.qs[1] + (int64_t)i * p.qs[2];
-    sQ[r][d] = __uint_as_float((unsigned)qrow[d] << 16);
+    sQ[r][d / 2] = (unsigned)qrow[d] | ((unsigned)qrow[d + 1] << 16);
   }
 
   // Issue this wave's key loads: instruction t covers keys j0 + 64 w + KPI t
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
   if (w == 0) {
     // |q|^2 of every packed row, by the same partial order and tree as q.k
     for (int r = kk; r < R; r += KPI) {
-      const float nq = group_sum<CB>(dot8(&sQ[r][8 * cb], &sQ[r][8 * cb]));
+      const float nq = group_sum<CB>(dot8(&sQ[r][4 * cb], &sQ[r][4 * cb]));
       if (cb == 0) sC[r][0] = nq;
     }
     if (lane < R) {
@@ -139,12 +144,12 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
   }
   __syncthreads();
 
-  // this lane's 8 columns of every packed query row
-  float qf[NR][8];
+  // this lane's 8 columns (4 bf16 pairs) of every packed query row
+  unsigned qf[NR][4];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qf[r][e] = r < R ? sQ[r][8 * cb + e] : 0.f;
+    for (int e = 0; e < 4; ++e) qf[r][e] = r < R ? sQ[r][4 * cb + e] : 0u;
 
   // Phase 1: scores and weights of this wave's 64 keys.
   float mx[NR];
@@ -153,12 +158,9 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
 #pragma unroll
   for (int t = 0; t < KIT; ++t) {
     const int jl = 64 * w + KPI * t + kk, j = j0 + jl;
-    float kf[8];
+    unsigned kf[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = bf_lo(kr[t][e]);
-      kf[2 * e + 1] = bf_hi(kr[t][e]);
-    }
+    for (int e = 0; e < 4; ++e) kf[e] = kr[t][e];
     const float nk = is_yat(VAR) ? group_sum<CB>(dot8(kf, kf)) : 0.f;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
