@@ -151,10 +151,22 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) qf[r][e] = r < R ? sQ[r][4 * cb + e] : 0u;
 
-  // Phase 1: scores and weights of this wave's 64 keys.
-  float mx[NR];
+  // Phase 1: scores and weights of this wave's 64 keys.  After the shuffle
+  // tree every one of a key's CB lanes holds its scores, so the map is spread
+  // over them: lane cb evaluates rows cb, cb + CB, ... (RPL of them) instead
+  // of every lane evaluating every row.
+  constexpr int RPL = (NR + CB - 1) / CB;
+  float mx[RPL], rnq[RPL], rc1[RPL], rc2[RPL];
+  int rqi[RPL];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) mx[r] = -INFINITY;
+  for (int q = 0; q < RPL; ++q) {
+    const int rr = cb + q * CB, rc = rr < R ? rr : 0;  // rows >= R: any valid row, unused
+    mx[q] = -INFINITY;
+    rnq[q] = sC[rc][0];
+    rc1[q] = sC[rc][1];
+    rc2[q] = sC[rc][2];
+    rqi[q] = rc - (rc / p.Tq) * p.Tq;
+  }
 #pragma unroll
   for (int t = 0; t < KIT; ++t) {
     const int jl = 64 * w + KPI * t + kk, j = j0 + jl;
@@ -162,36 +174,39 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) kf[e] = kr[t][e];
     const float nk = is_yat(VAR) ? group_sum<CB>(dot8(kf, kf)) : 0.f;
+    float sc[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (r < R) {
-        const float sc = group_sum<CB>(dot8(qf[r], kf));
-        const int i = r - (r / p.Tq) * p.Tq;
-        const bool ok = j < p.Tk && !(p.causal && j > i);
-        float val, m;
-        if (is_yat(VAR)) {
-          const float d2 = fmaf(-2.f, sc, sC[r][0] + nk);
-          const float kap = yat_numerator<VAR>(sc + sC[r][1], p.yat_power) *
-                            __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + sC[r][2]);
-          val = ok ? kap : 0.f;
-          m = ok ? kap : -INFINITY;
-        } else if (VAR == kSoftmax) {
-          const float x = sc * (scale * kLog2e);
-          val = ok ? x : -INFINITY;
-          m = val;
-        } else {
-          const float s = sc * scale;
-          const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
-          const float u1 = 1.f + e;
-          const float cc = (u1 - 1.f) - e;
-          const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - cc);
-          const float u = __builtin_amdgcn_exp2f(sC[r][1] * __builtin_amdgcn_logf(sp + 1e-6f));
-          val = ok ? u : 0.f;
-          m = ok ? s : -INFINITY;
-        }
-        if (cb == 0) sP[r][jl] = val;
-        mx[r] = fmaxf(mx[r], m);
+    for (int r = 0; r < NR; ++r) sc[r] = r < R ? group_sum<CB>(dot8(qf[r], kf)) : 0.f;
+#pragma unroll
+    for (int q = 0; q < RPL; ++q) {
+      const int rr = cb + q * CB;
+      float x = sc[0];
+#pragma unroll
+      for (int r = 1; r < NR; ++r) x = rr == r ? sc[r] : x;
+      const bool ok = rr < R && j < p.Tk && !(p.causal && j > rqi[q]);
+      float val, m;
+      if (is_yat(VAR)) {
+        const float d2 = fmaf(-2.f, x, rnq[q] + nk);
+        const float kap = yat_numerator<VAR>(x + rc1[q], p.yat_power) *
+                          __builtin_amdgcn_rcpf(fmaxf(d2, 0.f) + rc2[q]);
+        val = ok ? kap : 0.f;
+        m = ok ? kap : -INFINITY;
+      } else if (VAR == kSoftmax) {
+        const float xs = x * (scale * kLog2e);
+        val = ok ? xs : -INFINITY;
+        m = val;
+      } else {
+        const float s = x * scale;
+        const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
+        const float u1 = 1.f + e;
+        const float cc = (u1 - 1.f) - e;
+        const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - cc);
+        const float u = __builtin_amdgcn_exp2f(rc1[q] * __builtin_amdgcn_logf(sp + 1e-6f));
+        val = ok ? u : 0.f;
+        m = ok ? s : -INFINITY;
       }
+      if (rr < R) sP[rr][jl] = val;
+      mx[q] = fmaxf(mx[q], m);
     }
   }
   // Value loads for phase 3, issued now so that they overlap phase 2:
@@ -212,7 +227,9 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     if (r < R) {
-      float m = mx[r];
+      float m = -INFINITY;  // this lane's maximum of row r, if it maps row r
+#pragma unroll
+      for (int q = 0; q < RPL; ++q) m = cb + q * CB == r ? mx[q] : m;
 #pragma unroll
       for (int sh = 1; sh < 64; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
       if (lane == 0) sRed[w][r][0] = m;

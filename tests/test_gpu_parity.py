@@ -193,6 +193,10 @@ DECODE_FORCED = [
     (1, 2, 1, 1, 17000, 64, 64, False),     # 67 chunks: the merge reads more than 64
     (1, 2, 1, 1, 70001, 64, 32, False),     # 274 chunks, ragged last one
     (2, 3, 3, 1, 513, 32, 32, False),       # one row per kv head, ragged last chunk
+    (1, 8, 2, 1, 600, 16, 32, False),       # d_k = 16, 4 rows: each lane maps 2 rows
+    (1, 8, 1, 1, 300, 16, 16, False),       # d_k = 16, 8 rows: each lane maps 4 rows
+    (2, 4, 1, 2, 520, 32, 64, False),       # d_k = 32, 8 rows: each lane maps 2 rows
+    (1, 4, 1, 2, 2, 16, 16, True),          # causal, d_k = 16, 8 rows
 ]
 
 
@@ -207,7 +211,7 @@ def test_decode_kernel(variant, shape):
 
 def test_decode_kernel_tied_and_yat_options():
     # k := q puts the peak (|q|^2 + b)^2 / eps on the diagonal; the kernel's
-    # |q|^2, |k|^2 and q.k share one FMA order, so d2 is exactly 0 there
+    # |q|^2, |k|^2 and q.k share one v_dot2 order, so d2 is exactly 0 there
     inp = make_custom(1, 4, 4, 2, 2, 128, 128, "bf16", True, seed=24, qk_std=2.0, tied=True)
     full_check(inp, "yat", True, "decode_tied", block_rows=(8,))
     inp = make_custom(2, 8, 2, 1, 900, 128, 128, "bf16", False, seed=25, qk_std=1.0)
