@@ -17,7 +17,8 @@
 //            a fixed xor-shuffle tree; the map's weight goes to LDS;
 //   phase 2: per-row maximum and mass over the chunk (fixed-order reductions);
 //   phase 3: O = sum_j w_j v_j with the same lane split over value columns,
-//            the four key sub-rows added by shuffles and the waves in LDS.
+//            two keys per v_dot2 (bf16 weights), the four key sub-rows added
+//            by shuffles and the waves in LDS.
 // Each chunk writes unnormalised partials (O, mass, maximum, softmax
 // reference maximum) in the layout of the key-split path, and combine_partials
 // merges them.  Maps as in attn_bf16.hip ("Softmax-Free Attention in JAX/Flax
@@ -44,8 +45,6 @@ constexpr int kChunk = 256;  // keys per workgroup
 __device__ __forceinline__ u32x4 ld128_stream(rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
 }
-__device__ __forceinline__ float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
 // Sum over the N (2, 4, 8 or 16) lanes of an aligned group with DPP moves:
 // swap neighbours, swap pairs, then mirror within 8 and within 16 lanes.
@@ -271,21 +270,29 @@ __global__ __launch_bounds__(256) void attn_decode_bf16(Problem p) {
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+  // Two keys at a time (instructions t and t + 1 hold keys jl and jl + VPI in
+  // the same columns): each column's two values form one bf16 pair (one byte
+  // permute), the two weights another (rounded to bf16, as the matrix-core
+  // kernels weight the values), and one v_dot2 adds both products.
+  static_assert(VIT % 2 == 0, "key pairs");
 #pragma unroll
-  for (int t = 0; t < VIT; ++t) {
+  for (int t = 0; t < VIT; t += 2) {
     const int jl = 64 * w + VPI * t + vk;
-    float vf[8];
+    unsigned vp[8];  // column 2e: (key jl, key jl + VPI) pairs, then column 2e + 1
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      vf[2 * e] = bf_lo(vr[t][e]);
-      vf[2 * e + 1] = bf_hi(vr[t][e]);
+      vp[2 * e] = lo_halves(vr[t][e], vr[t + 1][e]);
+      vp[2 * e + 1] = hi_halves(vr[t][e], vr[t + 1][e]);
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       if (r < R) {
-        const float wv = sP[r][jl];  // 0 for keys past T_k (masked)
+        // 0 for keys past T_k (masked)
+        const bf16x2 wp = __builtin_bit_cast(bf16x2, pack_bf16(sP[r][jl], sP[r][jl + VPI]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[r][e] = fmaf(wv, vf[e], o[r][e]);
+        for (int e = 0; e < 8; ++e)
+          o[r][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vp[e]), wp,
+                                                    o[r][e], false);
       }
     }
   }
