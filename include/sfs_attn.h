@@ -37,6 +37,11 @@
  *     logit), over allowed keys.
  *   - s^tau is evaluated in one pass without a running maximum; its supported
  *     domain is tau * ln(phi) < 88 (no fp32 overflow of phi^tau).
+ *   - bf16 storage: the weights that multiply V are rounded to bf16 (the
+ *     matrix cores take bf16 operands; the decode kernel rounds the same way).
+ *     The Yat mass of the matrix-core kernels is the sum of those rounded
+ *     weights, so out is normalised by exactly the weights it averages with;
+ *     it differs from the fp32 sum of kappa by at most 2^-9 relative.
  */
 #ifndef SFS_ATTN_H
 #define SFS_ATTN_H
