@@ -50,11 +50,15 @@ def uses_decode_kernel(wl, args) -> bool:
 
 def kernels_timed(wl, args, variant) -> str:
     """The kernels one timed forward call runs: the decode kernel and its
-    merge, or the fused tile kernel after the |k|^2 pre-pass for Yat."""
+    merge, or the fused tile kernel after the |k|^2 pre-pass for Yat (at
+    d_k <= 32 the small-grid tile kernels form |k|^2 themselves)."""
     if uses_decode_kernel(wl, args):
         return f"attn_decode_bf16 ({variant}) + combine_partials"
-    pre = "|k|^2 pre-pass + " if variant == "yat" else ""
-    return f"{pre}attn_fwd_bf16 ({variant})"
+    if variant != "yat":
+        return f"attn_fwd_bf16 ({variant})"
+    if wl.dk <= 32:
+        return "attn_fwd_bf16 (yat; |k|^2 in-kernel in the small-grid kernels, else a pre-pass)"
+    return "|k|^2 pre-pass + attn_fwd_bf16 (yat)"
 
 
 def alg_bytes(wl) -> float:

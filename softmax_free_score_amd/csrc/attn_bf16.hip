@@ -90,6 +90,12 @@ __device__ __forceinline__ float yat_bias(const Problem& p, int h) {
   return p.yat_bias_free ? 0.f : softplus_precise(p.b_raw[h]);
 }
 
+// Yat with d_k <= 32 in the small-grid kernels: key norms formed in the
+// kernel (no pre-pass).
+__host__ __device__ constexpr bool yat_local_norms(int var, int dk) {
+  return is_yat(var) && dk <= 32;
+}
+
 // Yat pre-pass: (|k_j|^2 + b_h) 2^-96 for every key row and query head, by the same
 // MFMA sequence and start value as the score tile (see score_init).  One wave
 // per 32 rows; grid (ceil(T_k / 128), Hq, B), 256 threads; output
@@ -588,10 +594,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
   static_assert(BN % 32 == 0 && BN <= 64, "tiles are 32 or 64 keys");
 
+  // Yat with d_k <= 32 forms its key norms here, from the K fragments its
+  // score MFMAs read anyway: the same instruction, k-step order and start
+  // value as the pre-pass (ties still cancel), for KB KS more MFMAs per tile
+  // and wave instead of a pre-pass launch, which costs more at these widths.
+  constexpr bool NK_LOCAL = yat_local_norms(VAR, DK);
+
   // Two LDS stages: the tile being computed and the next one being filled.
   __shared__ __attribute__((aligned(16))) unsigned short sK[2][BN * KLD];
   __shared__ __attribute__((aligned(16))) unsigned short sV[2][DVP * VLD];
   __shared__ __attribute__((aligned(16))) float sNK[2][BN];
+  __shared__ __attribute__((aligned(16))) float sNKw[NK_LOCAL ? NW : 1][NK_LOCAL ? BN : 4];
   __shared__ float sNQ[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -696,7 +709,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         }
       }
     }
-    if (is_yat(VAR) && tid < BN / 4) nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
+    if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4)
+      nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
   };
 
   auto store_tile = [&](int buf) {
@@ -729,7 +743,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         }
       }
     }
-    if (is_yat(VAR) && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
+    if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
   };
 
   f32x16 o[DB];
@@ -761,6 +775,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
     }
+    f32x16 gk[NK_LOCAL ? KB : 1];  // NK_LOCAL: K K^T of each 32-key block, from b
+    if constexpr (NK_LOCAL) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) gk[kb] = sacc[kb];
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -768,7 +787,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, *(const u32x4*)&K[(kb * 32 + col) * KLD + 16 * s + 8 * half]);
         sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+        if constexpr (NK_LOCAL) gk[kb] = mfma32(a, a, gk[kb]);
       }
+    if constexpr (NK_LOCAL) {
+      // LDS row i of the tile holds key (i & ~31) | k_lds_row(i & 31); this
+      // wave's own copy of the norms, in key order (read back by the same wave)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        if (holds_diag(col, half))
+          sNKw[w][kb * 32 + k_lds_row(col)] = diag_of(gk[kb], col) * kNormScale;
+    }
 
     // key k0 + 8 half + o is allowed iff o <= lim (o: the element's offset,
     // a compile-time constant), so the mask is one compare per element
@@ -807,7 +835,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           mass += e;
         }
     } else if (is_yat(VAR)) {
-      const float* NK = sNK[buf];
+      const float* NK = NK_LOCAL ? sNKw[NK_LOCAL ? w : 0] : sNK[buf];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         // (read as float vectors: this compiler mis-evaluates a bit_cast of a
@@ -978,7 +1006,8 @@ template <int VAR, int DV>
 hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   constexpr int DK = SFS_DK;
   constexpr int BN = SFS_BN;
-  if (is_yat(VAR))
+  // (the small-grid kernels form the norms themselves at d_k <= 32)
+  if (is_yat(VAR) && !(p.block_rows != 256 && yat_local_norms(VAR, DK)))
     hipLaunchKernelGGL(yat_key_norms_bf16<DK>, dim3((p.Tk + 127) / 128, p.Hq, p.B), dim3(256), 0,
                        stream, p);
   // p.block_rows and p.kv_splits come from the host plan (make_plan)

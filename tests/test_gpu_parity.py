@@ -241,6 +241,8 @@ def test_decode_kernel_strided_gqa_determinism(variant):
     ((2, 4, 4, 200, 200, 128, 128), BLOCK_ROWS),     # every tile kernel
     ((1, 2, 2, 100, 100, 64, 32), BLOCK_ROWS),
     ((1, 4, 4, 2, 2, 128, 128), (8,)),               # the decode kernel
+    ((2, 6, 6, 256, 256, 32, 32), (64, 128)),        # small-grid kernels, norms formed in-kernel
+    ((1, 2, 2, 100, 100, 16, 16), (64, 128)),
 ])
 def test_yat_tied_keys_with_tiny_eps(shape, rows):
     """k := q and eps = softplus(-20) ~ 2e-9: the diagonal weight is
