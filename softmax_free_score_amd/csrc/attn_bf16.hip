@@ -203,30 +203,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   }
   const float scale = 1.0f / sqrtf((float)DK);
 
-  // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7].
+  // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7]
+  // (loaded in the prologue below).
   bf16x8 qf[KS];
-  {
-    const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
-                                     : q_bytes;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
-    // Drain these loads here: otherwise they are still outstanding on entry to
-    // the main loop, and every score MFMA there would wait for the tile loads
-    // issued after them.
-    __builtin_amdgcn_s_waitcnt(0);
-  }
   float nq = 0.f;
   // |k|^2 + b slice of this query head; padded to a multiple of 64 rows, so a
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
       is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;
   const f32x16 sinit = score_init<VAR>(bias);
-  if (is_yat(VAR)) {
-    f32x16 g = sinit;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
-    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
-  }
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
@@ -499,13 +484,29 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
       }
   };
 
-  // Prologue: K_0 into stage 0, K_1 and V_0 into the staging registers.
+  // Prologue: the query fragments and K_0 (group 0) or V_0 (group 1) in
+  // flight together, one wait for all of them (so that none is outstanding on
+  // entry to the main loop, where every score MFMA would otherwise wait for
+  // the tile loads issued after them); then |q|^2 + b, K_0 into stage 0 and
+  // K_1 into the staging registers.
+  {
+    const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
+                                     : q_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
+  }
+  if (grp == 0) load_k(0);
+  else load_v(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (is_yat(VAR)) {
+    f32x16 g = sinit;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
+    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
+  }
   if (grp == 0) {
-    load_k(0);
     store_k(0);
     if (n_tiles > 1) load_k(BN);
-  } else {
-    load_v(0);
   }
   __syncthreads();
   if (is_yat(VAR)) nq = sNQ[32 * w + col];
@@ -645,15 +646,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   }
   const float scale = 1.0f / sqrtf((float)DK);
 
-  // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7].
+  // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7]
+  // (loaded in the prologue below).
   bf16x8 qf[KS];
-  {
-    const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
-                                     : q_bytes;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
-    __builtin_amdgcn_s_waitcnt(0);  // not outstanding on entry to the main loop
-  }
   float nq = 0.f;
   // |k|^2 + b slice of this query head; padded to a multiple of 64 rows, so a
   // tile never reads past it (entries >= T_k are masked out).
@@ -661,12 +656,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;
   const f32x16 sinit = score_init<VAR>(bias);
   const int b_sgpr = __builtin_amdgcn_readfirstlane(__float_as_int(bias));
-  if (is_yat(VAR)) {
-    f32x16 g = sinit;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
-    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
-  }
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
@@ -912,9 +901,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       }
   };
 
-  // Prologue: the first tile into its stage, the next into registers.
+  // Prologue: the query fragments and the first tile in flight together, one
+  // wait for all of them (none outstanding on entry to the main loop); then
+  // |q|^2 + b, the first tile into its stage, the next into registers.
+  {
+    const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
+                                     : q_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
+  }
+  if (t_begin < t_end) load_tile(t_begin * BN);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (is_yat(VAR)) {
+    f32x16 g = sinit;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
+    if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
+  }
   if (t_begin < t_end) {
-    load_tile(t_begin * BN);
     store_tile(t_begin & 1);
     if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN);
   }
