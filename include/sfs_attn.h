@@ -161,6 +161,24 @@ int attn_fwd(const attn_desc* desc, const void* q, const void* k, const void* v,
              void* out, float* mass, float* max_score, void* workspace,
              size_t workspace_bytes, void* stream);
 
+/* Attention forward that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments,
+ * layouts, maps, asynchrony and errors are those of attn_fwd without the
+ * workspace: the scratch is a library-owned device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library is loaded on
+ * that GPU and held until the process ends.  A problem whose
+ * attn_fwd_workspace_bytes() exceeds that size returns ATTN_ERR_WORKSPACE
+ * (nothing enqueued).  Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents (no call relies on them): calls that may
+ * run concurrently on one GPU (different streams) race, so order them.
+ * Results are identical to attn_fwd's on the same inputs. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_fwd_noalloc(const attn_desc* desc, const void* q, const void* k, const void* v,
+                     int variant, const float* b_raw, const float* eps_raw,
+                     const float* log_tau, int causal, void* out, float* mass,
+                     float* max_score, void* stream);
+
 /* Yat kernel-family options.
  *
  * "The Kernel Between the Roles", section "The run": raising the power of the

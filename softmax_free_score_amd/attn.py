@@ -27,10 +27,12 @@ ATTN_F32, ATTN_BF16 = 0, 1
 VARIANTS = {"softmax": ATTN_SOFTMAX, "yat": ATTN_YAT, "stau": ATTN_STAU}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_UNSUPPORTED",
           -4: "ATTN_ERR_PARAM", -5: "ATTN_ERR_WORKSPACE", -6: "ATTN_ERR_HIP"}
-EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_yat",
+EXPORTS = ("attn_desc_init", "attn_fwd_workspace_bytes", "attn_fwd", "attn_fwd_noalloc",
+           "attn_fwd_yat",
            "attn_telemetry_workspace_bytes", "attn_telemetry", "attn_bwd_workspace_bytes",
            "attn_bwd", "attn_status_string", "attn_last_error")
 ATTN_YAT_MAX_POWER = 8
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnDesc(ctypes.Structure):
@@ -76,6 +78,9 @@ def load_library():
         lib.attn_fwd.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, ctypes.c_int, vp, vp, vp,
                                  ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, ctypes.c_int, vp,
+                                         vp, vp, ctypes.c_int, vp, vp, vp, vp]
+        lib.attn_fwd_noalloc.restype = ctypes.c_int
         lib.attn_fwd_yat.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp,
                                      ctypes.POINTER(AttnYatOpts), ctypes.c_int, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
@@ -147,7 +152,7 @@ def _ptr(t):
 
 
 def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_rows,
-             kv_splits=0):
+             kv_splits=0, allocate_workspace=True):
     lib = load_library()
     B, Hq, Tq, _ = q.shape
     dv = v.shape[3]
@@ -163,7 +168,7 @@ def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_ro
             raise ValueError(f"{name} must be a contiguous float32 tensor of B*Hq*Tq elements")
     desc = make_desc(q, k, v, out, block_rows, kv_splits)
     need = int(lib.attn_fwd_workspace_bytes(ctypes.byref(desc), variant))
-    if workspace is None and need > 0:
+    if workspace is None and need > 0 and allocate_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
@@ -187,6 +192,26 @@ def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=Fa
                       _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(out), _ptr(mass),
                       _ptr(max_score), _ptr(workspace), ws_bytes,
                       ctypes.c_void_p(stream) if stream else None)
+    if st != 0:
+        raise AttnError(st, lib.attn_last_error().decode())
+    return out, mass, max_score
+
+
+def attn_fwd_noalloc(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=False,
+                     out=None, mass=None, max_score=None, stream=None, block_rows=0,
+                     kv_splits=0):
+    """``attn_fwd`` without a workspace: the library's per-GPU scratch of
+    ATTN_NOALLOC_SCRATCH_BYTES serves instead, and the library allocates
+    nothing.  Outputs that are not given are allocated here, as in
+    ``attn_fwd``.  Calls that may overlap on one GPU race on the scratch."""
+    variant = VARIANTS.get(variant, variant)
+    lib, desc, out, mass, max_score, _, _, stream = _prepare(
+        q, k, v, variant, out, mass, max_score, None, stream, block_rows, kv_splits,
+        allocate_workspace=False)
+    st = lib.attn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), variant,
+                              _ptr(b_raw), _ptr(eps_raw), _ptr(log_tau), int(bool(causal)),
+                              _ptr(out), _ptr(mass), _ptr(max_score),
+                              ctypes.c_void_p(stream) if stream else None)
     if st != 0:
         raise AttnError(st, lib.attn_last_error().decode())
     return out, mass, max_score
@@ -219,6 +244,17 @@ def call_raw(desc: AttnDesc, q, k, v, variant, b_raw, eps_raw, log_tau, causal, 
     return int(lib.attn_fwd(dp, p(q), p(k), p(v), int(variant), p(b_raw),
                             p(eps_raw), p(log_tau), int(causal), p(out), p(mass), p(max_score),
                             p(workspace), int(workspace_bytes), p(stream)))
+
+
+def call_raw_noalloc(desc: AttnDesc, q, k, v, variant, b_raw, eps_raw, log_tau, causal, out,
+                     mass, max_score, stream) -> int:
+    """attn_fwd_noalloc with raw integer pointers (0 = NULL); returns the status."""
+    lib = load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    dp = ctypes.byref(desc) if desc is not None else None
+    return int(lib.attn_fwd_noalloc(dp, p(q), p(k), p(v), int(variant), p(b_raw), p(eps_raw),
+                                    p(log_tau), int(causal), p(out), p(mass), p(max_score),
+                                    p(stream)))
 
 
 def call_raw_yat(desc: AttnDesc, q, k, v, b_raw, eps_raw, opts, causal, out, mass, max_score,

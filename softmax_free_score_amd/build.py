@@ -38,6 +38,7 @@ def _units():
     units.append(("attn_f32", "attn_f32.hip", []))
     units.append(("attn_combine", "attn_combine.hip", []))
     units.append(("attn_bwd_aux", "attn_bwd_aux.hip", []))
+    units.append(("attn_scratch", "attn_scratch.hip", []))
     for dk in (16, 32, 64, 128):
         units.append((f"attn_bf16_dk{dk}", "attn_bf16.hip", [f"-DSFS_DK={dk}"]))
         units.append((f"attn_bwd_dk{dk}", "attn_bwd.hip", [f"-DSFS_DK={dk}"]))

@@ -279,6 +279,40 @@ int attn_fwd_yat(const attn_desc* d, const void* q, const void* k, const void* v
              max_score, workspace, workspace_bytes, stream);
 }
 
+int attn_fwd_noalloc(const attn_desc* d, const void* q, const void* k, const void* v,
+                     int variant, const float* b_raw, const float* eps_raw,
+                     const float* log_tau, int causal, void* out, float* mass,
+                     float* max_score, void* stream) {
+  // the same checks as attn_fwd, with the scratch size in place of the
+  // caller's workspace; nothing touches the GPU before they pass
+  bool empty = false;
+  const size_t need = d ? attn_fwd_workspace_bytes(d, variant) : 0;
+  int st = validate(d, q, k, v, variant, b_raw, eps_raw, log_tau, causal, out, mass, max_score,
+                    nullptr, 0, false, &empty, 0);
+  if (st != ATTN_OK || empty) return st;
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES) {
+    char msg[256];
+    std::snprintf(msg, sizeof msg,
+                  "attn_fwd_noalloc: this problem needs %zu bytes of scratch, more than the "
+                  "%u of ATTN_NOALLOC_SCRATCH_BYTES (use attn_fwd with a workspace)",
+                  need, (unsigned)ATTN_NOALLOC_SCRATCH_BYTES);
+    set_error(msg);
+    return ATTN_ERR_WORKSPACE;
+  }
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = sfs::scratch_address(&scratch);
+    if (e != hipSuccess) {
+      char msg[256];
+      std::snprintf(msg, sizeof msg, "HIP: %s (%s)", hipGetErrorName(e), hipGetErrorString(e));
+      set_error(msg);
+      return ATTN_ERR_HIP;
+    }
+  }
+  return run(d, q, k, v, variant, b_raw, eps_raw, log_tau, 1, 0, causal, out, mass, max_score,
+             scratch, need, stream);
+}
+
 size_t attn_telemetry_workspace_bytes(const attn_desc* d, int variant) {
   if (!d || d->dtype != ATTN_BF16) return 0;
   if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0) return 0;

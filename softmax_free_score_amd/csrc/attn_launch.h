@@ -134,6 +134,10 @@ struct Problem {
   int yat_bias_free;  // Yat: b = 0 exactly (b_raw not read)
 };
 
+// Device address of this GPU's scratch for attn_fwd_noalloc
+// (ATTN_NOALLOC_SCRATCH_BYTES), taken once per device (attn_scratch.hip).
+hipError_t scratch_address(void** ptr);
+
 // Telemetry pass: per-row entropy and sparsity of the weights, tau sums.
 hipError_t launch_stats_bf16_dk16(const Problem& p, hipStream_t stream);
 hipError_t launch_stats_bf16_dk32(const Problem& p, hipStream_t stream);

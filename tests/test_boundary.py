@@ -122,6 +122,35 @@ def test_workspace_rules():
     assert call(d, variant=attn.ATTN_YAT, ws=W + 4) == ERR_WS
 
 
+def call_noalloc(d, variant=attn.ATTN_SOFTMAX, causal=1, q=A, k=K, v=V, out=O, b=BR, e=ER,
+                 lt=LT, mass=M, mx=X):
+    return attn.call_raw_noalloc(d, q, k, v, variant, b, e, lt, causal, out, mass, mx, 0)
+
+
+def test_noalloc_rules():
+    lib = attn.load_library()
+    # 64 batches x 64 query heads x 4096 keys of |k|^2 + b: 64 MiB > the scratch
+    big = desc(B=64, Hq=64, Hkv=64, Tq=4096, Tk=4096, dk=128, dv=128)
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(big), attn.ATTN_YAT) > \
+        attn.ATTN_NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(big, variant=attn.ATTN_YAT) == ERR_WS
+    assert "ATTN_NOALLOC_SCRATCH_BYTES" in lib.attn_last_error().decode()
+    # the ordinary checks come first, as in attn_fwd
+    assert call_noalloc(None) == ERR_NULL
+    assert call_noalloc(desc(), out=0) == ERR_NULL
+    assert call_noalloc(desc(Tq=64, Tk=32)) == ERR_SHAPE
+    assert call_noalloc(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
+    assert call_noalloc(desc(B=0), q=0, k=0, v=0, out=0) == OK
+
+
+def test_noalloc_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert call_noalloc(desc(), variant=attn.ATTN_YAT) == ERR_HIP
+    assert call_noalloc(desc(), variant=attn.ATTN_SOFTMAX) == ERR_HIP
+
+
 def test_empty_problem_is_a_no_op():
     assert call(desc(B=0), q=0, k=0, v=0, out=0) == OK
     assert call(desc(Tq=0, Tk=5), causal=0, q=0, k=0, v=0, out=0) == OK
