@@ -212,9 +212,8 @@ int attn_fwd_yat(const attn_desc* desc, const void* q, const void* k, const void
  * row statistics that forward returned.  The weights of every allowed pair are
  * recomputed as the forward defines them, and the pass returns:
  *   row_entropy   [B,Hq,Tq]: -sum_j w_ij ln w_ij / ln(n_i) over the n_i allowed
- *                 keys, 0 when n_i = 1 ("The Kernel Between the Roles", "What
- *                 each normalizer forgets": 0 for a row on one key, 1 for
- *                 uniform weights);
+ *                 keys, 0 when n_i = 1 ("The Kernel Between the Roles", "The
+ *                 run": 0 for a row on one key, 1 for uniform weights);
  *   row_sparsity  [B,Hq,Tq]: the fraction of allowed keys with w_ij below
  *                 sparsity_threshold (the s^tau post measures weights < 1e-6);
  *   tau_star      [Hq]: Cov(s, ln phi(s)) / Var(ln phi(s)) over all allowed

@@ -77,9 +77,12 @@ def build(verbose: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        path = os.environ.get("SFS_ORACLE_LIBRARY")   # another build of the same source
+        if not path:
+            path = _LIB_PATH
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+                build()
+        lib = ctypes.CDLL(path)
         d = ctypes.POINTER(ctypes.c_double)
         i64 = ctypes.c_int64
         lib.oracle_attn_fwd.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64,
@@ -210,7 +213,7 @@ def telemetry_np(q, k, variant, b_raw=None, eps_raw=None, log_tau=None, causal=F
     * row_entropy: the entropy of the row's weights over its allowed keys,
       -sum w ln w, divided by ln(n) for n allowed keys (0 for n = 1): 0 for a
       row that puts everything on one key, 1 for uniform weights ("The Kernel
-      Between the Roles", "What each normalizer forgets").
+      Between the Roles", "The run").
     * row_sparsity: the fraction of allowed keys whose weight is below the
       threshold (the s^tau post's sparsity, weights < 1e-6).
     * tau_star: per query head, Cov(s, ln phi(s)) / Var(ln phi(s)) over every

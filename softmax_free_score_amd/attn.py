@@ -15,12 +15,16 @@ accepted.  b_raw, eps_raw and log_tau are float32 [Hq] device tensors.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfs_attn.so")
+# SFS_ATTN_LIBRARY names another build of the same library (e.g. the host
+# code built with sanitizers); by default the in-tree one is loaded.
+_LIB_PATH = os.environ.get("SFS_ATTN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libsfs_attn.so")
 
 ATTN_SOFTMAX, ATTN_YAT, ATTN_STAU = 0, 1, 2
 ATTN_F32, ATTN_BF16 = 0, 1
@@ -151,28 +155,110 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_qkv(q, k, v=None):
+    """q, k (and v): 4-D tensors of one supported dtype on one device."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor [B, H, T, d]")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} is {t.dtype}, q is {q.dtype}: they must match")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}: they must match")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
+
+
+def _check_f32(name, t, device, numel, exact=False):
+    """A float32 contiguous tensor on ``device`` of ``numel`` elements (at least
+    ``numel`` unless ``exact``); None passes (the library checks presence)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise ValueError(f"{name} must be a float32 tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}: they must match")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if (t.numel() != numel) if exact else (t.numel() < numel):
+        want = "exactly" if exact else "at least"
+        raise ValueError(f"{name} has {t.numel()} elements, needs {want} {numel}")
+
+
+def _check_params(q, Hq, b_raw, eps_raw, log_tau):
+    for name, t in (("b_raw", b_raw), ("eps_raw", eps_raw), ("log_tau", log_tau)):
+        _check_f32(name, t, q.device, Hq)
+
+
+def _check_like(name, t, shape, dtype, device):
+    """An output tensor given by the caller: this shape, dtype and device, last
+    axis contiguous (other strides are the library's to check)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape):
+        got = tuple(t.shape) if isinstance(t, torch.Tensor) else type(t).__name__
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {got}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}: they must match")
+
+
+def _check_workspace(workspace, device):
+    if workspace is None:
+        return
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError("workspace must be a tensor on q's device")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _check_on_gpu(q):
+    if not q.is_cuda:
+        raise ValueError(f"tensors are on {q.device}: the library needs GPU (HIP) device memory")
+
+
+def _stream_handle(stream, device):
+    """(raw stream handle, allocation context): tensors allocated here for a
+    call on a stream other than torch's current one are allocated on that
+    stream, so the caching allocator does not hand their memory to other work
+    before the call's kernels are done with it."""
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream, contextlib.nullcontext()
+    handle = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+    if handle == torch.cuda.current_stream(device).cuda_stream:
+        return handle, contextlib.nullcontext()
+    return handle, torch.cuda.stream(torch.cuda.ExternalStream(handle, device=device))
+
+
 def _prepare(q, k, v, variant, out, mass, max_score, workspace, stream, block_rows,
-             kv_splits=0, allocate_workspace=True):
-    lib = load_library()
+             kv_splits=0, allocate_workspace=True, params=(None, None, None)):
+    # every check on the arguments comes before the first library call
+    _check_qkv(q, k, v)
     B, Hq, Tq, _ = q.shape
     dv = v.shape[3]
-    if out is None:
-        out = torch.empty((B, Hq, Tq, dv), dtype=q.dtype, device=q.device)
-    if mass is None:
-        mass = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
-    if max_score is None:
-        max_score = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
-    for name, t in (("mass", mass), ("max_score", max_score)):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
-                              or t.numel() != B * Hq * Tq):
-            raise ValueError(f"{name} must be a contiguous float32 tensor of B*Hq*Tq elements")
+    _check_like("out", out, (B, Hq, Tq, dv), q.dtype, q.device)
+    _check_f32("mass", mass, q.device, B * Hq * Tq, exact=True)
+    _check_f32("max_score", max_score, q.device, B * Hq * Tq, exact=True)
+    _check_params(q, Hq, *params)
+    _check_workspace(workspace, q.device)
     desc = make_desc(q, k, v, out, block_rows, kv_splits)
+    _check_on_gpu(q)
+    lib = load_library()
+    stream, alloc = _stream_handle(stream, q.device)
     need = int(lib.attn_fwd_workspace_bytes(ctypes.byref(desc), variant))
-    if workspace is None and need > 0 and allocate_workspace:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with alloc:
+        if out is None:
+            out = torch.empty((B, Hq, Tq, dv), dtype=q.dtype, device=q.device)
+            desc = make_desc(q, k, v, out, block_rows, kv_splits)
+        if mass is None:
+            mass = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+        if max_score is None:
+            max_score = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+        if workspace is None and need > 0 and allocate_workspace:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
     return lib, desc, out, mass, max_score, workspace, ws_bytes, stream
 
 
@@ -187,7 +273,8 @@ def attn_fwd(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, causal=Fa
     on q's device.  Raises AttnError with the library's status on failure."""
     variant = VARIANTS.get(variant, variant)
     lib, desc, out, mass, max_score, workspace, ws_bytes, stream = _prepare(
-        q, k, v, variant, out, mass, max_score, workspace, stream, block_rows, kv_splits)
+        q, k, v, variant, out, mass, max_score, workspace, stream, block_rows, kv_splits,
+        params=(b_raw, eps_raw, log_tau))
     st = lib.attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), variant, _ptr(b_raw),
                       _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(out), _ptr(mass),
                       _ptr(max_score), _ptr(workspace), ws_bytes,
@@ -207,7 +294,7 @@ def attn_fwd_noalloc(q, k, v, variant, b_raw=None, eps_raw=None, log_tau=None, c
     variant = VARIANTS.get(variant, variant)
     lib, desc, out, mass, max_score, _, _, stream = _prepare(
         q, k, v, variant, out, mass, max_score, None, stream, block_rows, kv_splits,
-        allocate_workspace=False)
+        allocate_workspace=False, params=(b_raw, eps_raw, log_tau))
     st = lib.attn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), variant,
                               _ptr(b_raw), _ptr(eps_raw), _ptr(log_tau), int(bool(causal)),
                               _ptr(out), _ptr(mass), _ptr(max_score),
@@ -224,7 +311,8 @@ def attn_fwd_yat(q, k, v, b_raw=None, eps_raw=None, power=1, bias_free=False, ca
     and b = 0 exactly when ``bias_free`` (b_raw then unused).  Otherwise as
     ``attn_fwd(..., "yat", ...)``."""
     lib, desc, out, mass, max_score, workspace, ws_bytes, stream = _prepare(
-        q, k, v, ATTN_YAT, out, mass, max_score, workspace, stream, block_rows, kv_splits)
+        q, k, v, ATTN_YAT, out, mass, max_score, workspace, stream, block_rows, kv_splits,
+        params=(b_raw, eps_raw, None))
     opts = AttnYatOpts(int(power), int(bool(bias_free)))
     st = lib.attn_fwd_yat(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(b_raw),
                           _ptr(eps_raw), ctypes.byref(opts), int(bool(causal)), _ptr(out),
@@ -277,20 +365,26 @@ def attn_telemetry(q, k, variant, mass, max_score=None, b_raw=None, eps_raw=None
     (row_entropy [B,Hq,Tq], row_sparsity [B,Hq,Tq], tau_star [Hq]) as float32
     device tensors (None for the ones not asked for).  ``mass`` and
     ``max_score`` are the forward's outputs."""
-    lib = load_library()
     variant = VARIANTS.get(variant, variant)
+    _check_qkv(q, k)
     B, Hq, Tq, _ = q.shape
+    _check_f32("mass", mass, q.device, B * Hq * Tq, exact=True)
+    _check_f32("max_score", max_score, q.device, B * Hq * Tq, exact=True)
+    _check_params(q, Hq, b_raw, eps_raw, log_tau)
+    _check_workspace(workspace, q.device)
     desc = make_desc(q, k, k, q)   # v and out are not used; k and q give valid shapes
+    _check_on_gpu(q)
+    lib = load_library()
+    stream, alloc = _stream_handle(stream, q.device)
     f32 = dict(dtype=torch.float32, device=q.device)
-    ent = torch.empty((B, Hq, Tq), **f32) if entropy else None
-    spa = torch.empty((B, Hq, Tq), **f32) if sparsity else None
-    tau = torch.empty((Hq,), **f32) if tau_star else None
     need = int(lib.attn_telemetry_workspace_bytes(ctypes.byref(desc), variant))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with alloc:
+        ent = torch.empty((B, Hq, Tq), **f32) if entropy else None
+        spa = torch.empty((B, Hq, Tq), **f32) if sparsity else None
+        tau = torch.empty((Hq,), **f32) if tau_star else None
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
     st = lib.attn_telemetry(ctypes.byref(desc), _ptr(q), _ptr(k), variant, _ptr(b_raw),
                             _ptr(eps_raw), _ptr(log_tau), int(bool(causal)), _ptr(mass),
                             _ptr(max_score), float(sparsity_threshold), _ptr(ent), _ptr(spa),
@@ -316,31 +410,36 @@ def attn_bwd(q, k, v, dout, variant, mass, max_score=None, b_raw=None, eps_raw=N
     Yat, dlog_tau for s^tau; float32 [Hq]).  ``mass`` and ``max_score`` are
     the forward's row statistics (softmax needs both, s^tau the mass; Yat
     reads neither and takes None); ``dout`` is dL/dout [B, Hq, Tq, dv]."""
-    lib = load_library()
     variant = VARIANTS.get(variant, variant)
+    _check_qkv(q, k, v)
     B, Hq, Tq, _ = q.shape
-    if dout.dim() != 4 or tuple(dout.shape) != (B, Hq, Tq, v.shape[3]):
-        raise ValueError("dout must be [B, Hq, Tq, dv]")
-    grads = {}
+    _check_like("dout", dout, (B, Hq, Tq, v.shape[3]), q.dtype, q.device)
     for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t is None:
-            t = torch.empty_strided(like.shape, like.stride(), dtype=like.dtype,
-                                    device=like.device)
-        elif t.shape != like.shape or t.stride() != like.stride() or t.dtype != like.dtype:
-            raise ValueError(f"{name} must have the shape, strides and dtype of its input")
-        grads[name] = t
+        _check_like(name, t, like.shape, like.dtype, like.device)
+        if t is not None and t.stride() != like.stride():
+            raise ValueError(f"{name} must have the strides of its input")
+    _check_f32("mass", mass, q.device, B * Hq * Tq, exact=True)
+    _check_f32("max_score", max_score, q.device, B * Hq * Tq, exact=True)
+    _check_params(q, Hq, b_raw, eps_raw, log_tau)
+    _check_workspace(workspace, q.device)
+    desc = make_desc(q, k, v, dout)
+    _check_on_gpu(q)
+    lib = load_library()
+    stream, alloc = _stream_handle(stream, q.device)
+    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc), variant))
     f32 = dict(dtype=torch.float32, device=q.device)
     want_p = bool(param_grads)
-    grads["db_raw"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_YAT else None
-    grads["deps_raw"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_YAT else None
-    grads["dlog_tau"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_STAU else None
-    desc = make_desc(q, k, v, dout)
-    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(desc), variant))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    grads = {}
+    with alloc:
+        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            grads[name] = t if t is not None else torch.empty_strided(
+                like.shape, like.stride(), dtype=like.dtype, device=like.device)
+        grads["db_raw"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_YAT else None
+        grads["deps_raw"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_YAT else None
+        grads["dlog_tau"] = torch.empty(Hq, **f32) if want_p and variant == ATTN_STAU else None
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
     st = lib.attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                       variant, _ptr(b_raw), _ptr(eps_raw), _ptr(log_tau), int(bool(causal)),
                       _ptr(mass), _ptr(max_score), _ptr(grads["dq"]), _ptr(grads["dk"]),

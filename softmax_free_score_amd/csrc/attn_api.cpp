@@ -36,6 +36,23 @@ bool strides_ok(const int64_t s[3], int64_t rows, int64_t d, int64_t elem) {
   return span < (int64_t(1) << 31);
 }
 
+// Sizes whose index and workspace arithmetic cannot overflow: every extent
+// within 32 bits, B*Hq*Tq query rows within 32 bits, B*Hq*Tk within 2^40 and
+// head sizes within 4096 (no kernel is built for more).  Tq may be 0 here.
+bool sizes_fit(const attn_desc* d) {
+  if (d->B < 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq < 0 || d->Tk <= 0 || d->dk <= 0 ||
+      d->dv <= 0)
+    return false;
+  if (d->B > INT32_MAX || d->Hq > INT32_MAX || d->Tq > INT32_MAX || d->Tk > INT32_MAX ||
+      d->dk > 4096 || d->dv > 4096)
+    return false;
+  int64_t bh = 0, rows_q = 0, rows_k = 0;
+  if (__builtin_mul_overflow(d->B, d->Hq, &bh) || __builtin_mul_overflow(bh, d->Tq, &rows_q) ||
+      __builtin_mul_overflow(bh, d->Tk, &rows_k))
+    return false;
+  return rows_q <= INT32_MAX && rows_k <= (int64_t(1) << 40);
+}
+
 // Workspace layout of the bf16 path: Yat |k|^2 rows, then (key splits) the
 // partials, each region 256-byte aligned.
 struct WsLayout {
@@ -87,9 +104,9 @@ int validate(const attn_desc* d, const void* q, const void* k, const void* v, in
     set_error("a causal mask needs Tq == Tk");
     return ATTN_ERR_SHAPE;
   }
-  if (d->B > INT32_MAX || d->Hq > INT32_MAX || d->Tq > INT32_MAX || d->Tk > INT32_MAX ||
-      d->B * d->Hq * d->Tq > INT32_MAX) {
-    set_error("problem too large for 32-bit row indices");
+  if (!sizes_fit(d)) {
+    set_error("problem too large (B*Hq*Tq and each extent within 32 bits, B*Hq*Tk within "
+              "2^40, head sizes within 4096)");
     return ATTN_ERR_UNSUPPORTED;
   }
   if (variant < ATTN_SOFTMAX || variant > ATTN_STAU) {
@@ -174,8 +191,7 @@ int attn_desc_init(attn_desc* d, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq,
 }
 
 size_t attn_fwd_workspace_bytes(const attn_desc* d, int variant) {
-  if (!d || d->dtype != ATTN_BF16) return 0;
-  if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0 || d->dv <= 0) return 0;
+  if (!d || d->dtype != ATTN_BF16 || !sizes_fit(d) || d->B == 0 || d->Tq == 0) return 0;
   return ws_need(d, variant);
 }
 
@@ -314,8 +330,7 @@ int attn_fwd_noalloc(const attn_desc* d, const void* q, const void* k, const voi
 }
 
 size_t attn_telemetry_workspace_bytes(const attn_desc* d, int variant) {
-  if (!d || d->dtype != ATTN_BF16) return 0;
-  if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0) return 0;
+  if (!d || d->dtype != ATTN_BF16 || !sizes_fit(d) || d->B == 0 || d->Tq == 0) return 0;
   const size_t nk = variant == ATTN_YAT ? (size_t)(d->B * d->Hkv * sfs::nk_pitch(d->Tk)) * 4 : 0;
   const size_t n_qt = (size_t)((d->Tq + sfs::kStatsRows - 1) / sfs::kStatsRows);
   return (nk + 255) / 256 * 256 + (size_t)(d->Hq * d->B) * n_qt * 8 * sizeof(double);
@@ -425,8 +440,7 @@ BwdWs bwd_ws(const attn_desc* d, int variant) {
 extern "C" {
 
 size_t attn_bwd_workspace_bytes(const attn_desc* d, int variant) {
-  if (!d || d->dtype != ATTN_BF16) return 0;
-  if (d->B <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->Tq <= 0 || d->Tk <= 0) return 0;
+  if (!d || d->dtype != ATTN_BF16 || !sizes_fit(d) || d->B == 0 || d->Tq == 0) return 0;
   if (variant < ATTN_SOFTMAX || variant > ATTN_STAU) return 0;
   return bwd_ws(d, variant).total;
 }

@@ -23,8 +23,8 @@ namespace {
 // tile) it accumulates the sums that give tau* = Cov(s, ln phi(s)) /
 // Var(ln phi(s)) with s = q.k / sqrt(d_k), phi = softplus(s) + 1e-6 (the s^tau
 // post's closed form), whatever the branch.  Entropy is normalised by ln n
-// ("The Kernel Between the Roles", "What each normalizer forgets": 0 for a row
-// on one key, 1 for uniform weights).  64 query rows per workgroup (2 waves),
+// ("The Kernel Between the Roles", "The run": 0 for a row on one key, 1 for
+// uniform weights).  64 query rows per workgroup (2 waves),
 // 32-key tiles staged through LDS; the score tile and its layout are those of
 // the forward.
 template <int VAR, int DK>

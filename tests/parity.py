@@ -5,9 +5,12 @@ Tolerances (fixed here, derived from the stated bar):
   fp32 storage: out max|d| <= 1e-5 * max|ref| (normwise over the tensor);
                 mass |d| <= 1e-5 * |ref| per row;
                 max_score |d| <= 1e-5 * |ref| + 1e-6 * max|ref| per row.
-  bf16 storage: out max|d| <= 2e-2 * max|V| (the value scale: every output
-                row is a convex combination of value rows), and the mean
-                |d| <= 5e-3 * rms(V);
+  bf16 storage: out, element by element, |d| <= 2e-2 * rms(V) + 2^-7 * |ref|:
+                the first term covers the weights rounded to bf16 before the
+                value contraction (2^-9 relative per weight, averaged over the
+                keys of a row), the second the output's own rounding to bf16
+                (at most 2^-9 relative) with room for the fp32 sums; and the
+                mean |d| over the tensor <= 5e-3 * rms(V);
                 mass |d| <= 1e-2 * |ref| per row;
                 max_score |d| <= 1e-2 * |ref| + 1e-3 * max|ref| per row.
 """
@@ -21,7 +24,7 @@ from softmax_free_score_amd import attn
 
 TOL = {
     "f32": dict(out=1e-5, mass=1e-5, mx=1e-5, mx_floor=1e-6),
-    "bf16": dict(out=2e-2, mass=1e-2, mx=1e-2, mx_floor=1e-3),
+    "bf16": dict(out=2e-2, out_rel=2.0 ** -7, mean=5e-3, mass=1e-2, mx=1e-2, mx_floor=1e-3),
 }
 
 
@@ -76,40 +79,34 @@ def oracle_rows(inp, variant, causal, rows, yat_opts=None):
                              **{n: a.astype(np.float64) for n, a in inp.params().items()})
 
 
-def check(dtype, got, ref, v_scale, label="", v_rms=None):
+def check(dtype, got, ref, label="", v_rms=None):
     """got, ref: (out, mass, max_score) as float64 arrays of equal shape.
-    v_scale: max|V| (bf16) -- the scale the output error is measured in."""
+    v_rms: rms of the values (bf16): the scale of the output bound."""
     tol = TOL[dtype]
     out_g, mass_g, mx_g = got
     out_r, mass_r, mx_r = ref
     assert np.all(np.isfinite(out_g)) and np.all(np.isfinite(mass_g)) and np.all(np.isfinite(mx_g)), \
         f"{label}: non-finite GPU output"
-    d_out = np.abs(out_g - out_r).max() if out_r.size else 0.0
-    scale = v_scale if dtype == "bf16" else max(np.abs(out_r).max(), 1e-30)
-    e_out = d_out / scale
+    e_mean = 0.0
+    if not out_r.size:
+        e_out = 0.0
+    elif dtype == "bf16":
+        assert v_rms is not None and v_rms > 0, "the bf16 bound needs rms(V)"
+        diff = np.abs(out_g - out_r)
+        e_out = (diff / (tol["out"] * v_rms + tol["out_rel"] * np.abs(out_r))).max()
+        e_mean = diff.mean() / v_rms
+        e_abs = diff.max() / v_rms
+    else:
+        e_out = np.abs(out_g - out_r).max() / (tol["out"] * max(np.abs(out_r).max(), 1e-30))
     e_mass = (np.abs(mass_g - mass_r) / np.maximum(np.abs(mass_r), 1e-30)).max()
     mx_bound = tol["mx"] * np.abs(mx_r) + tol["mx_floor"] * np.abs(mx_r).max()
     e_mx = (np.abs(mx_g - mx_r) / np.maximum(mx_bound, 1e-30)).max()
-    e_mean = 0.0
-    if dtype == "bf16" and v_rms is not None and out_r.size:
-        e_mean = np.abs(out_g - out_r).mean() / v_rms
-    say(f"  {label}: out err {e_out:.3e} (tol {tol['out']:.0e}), mean {e_mean:.2e}, "
+    extra = f" (max|d| {e_abs:.2e} rms(V))" if dtype == "bf16" and out_r.size else ""
+    say(f"  {label}: out err/bound {e_out:.3f}{extra}, mean {e_mean:.2e} rms(V), "
         f"mass rel err {e_mass:.3e} (tol {tol['mass']:.0e}), max_score err/bound {e_mx:.3f}")
-    assert e_out <= tol["out"], f"{label}: out error {e_out:.3e} > {tol['out']}"
-    assert e_mean <= 5e-3, f"{label}: mean out error {e_mean:.3e} > 5e-3 rms(V)"
+    assert e_out <= 1.0, f"{label}: out error outside its bound (ratio {e_out:.3f})"
+    if dtype == "bf16":
+        assert e_mean <= tol["mean"], f"{label}: mean out error {e_mean:.3e} > 5e-3 rms(V)"
     assert e_mass <= tol["mass"], f"{label}: mass error {e_mass:.3e} > {tol['mass']}"
     assert e_mx <= 1.0, f"{label}: max_score outside bound (ratio {e_mx:.3f})"
     return e_out, e_mass
-
-
-def sample_rows(B, Hq, Tq, n_random=256, seed=123):
-    """Flat row ids: corners, tile edges and a seeded random set."""
-    rng = np.random.default_rng(seed)
-    edges = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, Tq - 2, Tq - 1]
-    rows = set()
-    for i in edges:
-        if 0 <= i < Tq:
-            rows.add(i)                                   # b = 0, h = 0
-            rows.add(((B - 1) * Hq + Hq - 1) * Tq + i)    # last b, last h
-    rows.update(rng.integers(0, B * Hq * Tq, n_random).tolist())
-    return np.array(sorted(rows), dtype=np.int64)

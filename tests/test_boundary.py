@@ -151,6 +151,29 @@ def test_noalloc_without_device_reports_hip_error():
     assert call_noalloc(desc(), variant=attn.ATTN_SOFTMAX) == ERR_HIP
 
 
+@pytest.mark.parametrize("B,Hq,Tq,Tk", [
+    (2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1),   # products overflow int64
+    (2 ** 31, 1, 1, 1),                                     # an extent past 32 bits
+    (2 ** 16, 2 ** 8, 2 ** 8, 2 ** 8),                      # 2^32 query rows
+    (2 ** 10, 2 ** 10, 1, 2 ** 21),                         # 2^41 key rows
+])
+def test_oversized_problems_are_refused(B, Hq, Tq, Tk):
+    lib = attn.load_library()
+    d = attn.AttnDesc()
+    assert lib.attn_desc_init(ctypes.byref(d), 1, 1, 1, 1, 1, 64, 64, attn.ATTN_BF16) == OK
+    d.B, d.Hq, d.Hkv, d.Tq, d.Tk = B, Hq, 1, Tq, Tk
+    for variant in (attn.ATTN_SOFTMAX, attn.ATTN_YAT, attn.ATTN_STAU):
+        assert lib.attn_fwd_workspace_bytes(ctypes.byref(d), variant) == 0
+        assert lib.attn_bwd_workspace_bytes(ctypes.byref(d), variant) == 0
+        assert lib.attn_telemetry_workspace_bytes(ctypes.byref(d), variant) == 0
+        assert call(d, variant=variant, causal=0) == ERR_UNSUP
+        assert call_noalloc(d, variant=variant, causal=0) == ERR_UNSUP
+    d.dk = d.dv = 8192
+    d.B, d.Hq, d.Tq, d.Tk = 1, 1, 1, 1
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(d), attn.ATTN_YAT) == 0
+    assert call(d, variant=attn.ATTN_YAT) == ERR_UNSUP
+
+
 def test_empty_problem_is_a_no_op():
     assert call(desc(B=0), q=0, k=0, v=0, out=0) == OK
     assert call(desc(Tq=0, Tk=5), causal=0, q=0, k=0, v=0, out=0) == OK

@@ -480,8 +480,8 @@ def test_oracle_rejects_bad_arguments():
 
 
 # --------------------------------------------------------------------------
-# Telemetry: normalised row entropy ("The Kernel Between the Roles", "What
-# each normalizer forgets"), sparsity and tau* (the s^tau post)
+# Telemetry: normalised row entropy ("The Kernel Between the Roles", "The
+# run"), sparsity and tau* (the s^tau post)
 
 def tel(q, k, variant, causal=False, **kw):
     q, k = np.asarray(q, float)[None, None], np.asarray(k, float)[None, None]
