@@ -305,8 +305,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
   f32x16 sacc[KB];          // S_t, from M(t) to W(t)
   bf16x8 pb[KB][2];         // P_t in bf16, from W(t) to M(t+1)
-  float mass = 0.f;         // Yat, s^tau: sum of weights; softmax: sum exp2(x - mref)
-  float mx = -INFINITY;     // Yat: max kappa; s^tau: max s; softmax: max of x = s*log2e/sqrt(dk)
+  float mass = 0.f;         // Yat: sum of weights; s^tau: of weights / (ln 2)^tau; softmax: sum exp2(x - mref)
+  float mx = -INFINITY;     // Yat: max kappa; s^tau: max q.k; softmax: max of x = s*log2e/sqrt(dk)
   float mref = -INFINITY;   // softmax: reference maximum of the exponentials
   const float c_sm = scale * kLog2e;
 
@@ -442,29 +442,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           }
         }
       }
-    } else {  // s^tau
+    } else {  // s^tau: weights phi^tau / (ln 2)^tau; max_score tracked on q.k
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sacc[kb][r] * scale;
-          // softplus(s) = max(s, 0) + log1p(e), e = exp(-|s|) in (0, 1].  The
-          // rounding error c of u1 = 1 + e is exact (u1 - 1 - e); log1p(e) =
-          // ln(u1) - c/u1 to first order, and c/u1 = c within a relative e.
-          const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
-          const float u1 = 1.f + e;
-          const float c = (u1 - 1.f) - e;
-          const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
-          float u = __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(sp + 1e-6f));
-          float sm = s;
+          const float x = sacc[kb][r];
+          float u = stau_weight2(x, c_sm, tau);
+          float xm = x;
           if (MASK) {
             const bool ok = allowed(kb, r);
             u = ok ? u : 0.f;
-            sm = ok ? s : -INFINITY;
+            xm = ok ? x : -INFINITY;
           }
           sacc[kb][r] = u;
           mass += u;
-          mx = fmaxf(mx, sm);
+          mx = fmaxf(mx, xm);
         }
     }
 #pragma unroll
@@ -567,8 +560,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
       }
     if (half == 0) {
       const int64_t ri = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
-      if (p.mass) p.mass[ri] = mass_all;
-      if (p.max_score) p.max_score[ri] = VAR == kSoftmax ? mx_all * kLn2 : mx_all;
+      if (p.mass) p.mass[ri] = VAR == kStau ? mass_all * stau_unit(tau) : mass_all;
+      if (p.max_score)
+        p.max_score[ri] = VAR == kSoftmax ? mx_all * kLn2 : VAR == kStau ? mx_all * scale : mx_all;
     }
   }
 }
@@ -577,7 +571,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 // kernel needs to fill and balance the chip): NW waves x 32 query rows per
 // workgroup, several workgroups per CU, one 64- or 32-key tile per iteration
 // with two LDS stages.  Same layouts and score -> weight maps as above.
-template <int VAR, int DK, int DV, int NW, int BN>
+// PRE: every workgroup has at most kPreTiles tiles (short key ranges).  The
+// prologue then issues all of its tile loads at once, next to the query
+// fragments, and stores them to kPreTiles LDS stages: one memory latency per
+// workgroup instead of one per tile, and no barrier inside the tile loop.
+// It pays where the map is cheap (softmax); where the map is long (Yat,
+// s^tau) the two-stage pipeline, which starts on the first tile while the
+// next one loads, is as fast or faster, so the launcher keeps it there.
+constexpr int kPreTiles = 4;
+
+template <int VAR, int DK, int DV, int NW, int BN, bool PRE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_small(Problem p) {
   constexpr int BM = NW * 32;            // query rows per workgroup
@@ -594,6 +597,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   constexpr int V_UNITS = (BN / 4) * (DV / 8);  // 4 keys x 8 values each
   constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
   static_assert(BN % 32 == 0 && BN <= 64, "tiles are 32 or 64 keys");
+  constexpr int NSTG = PRE ? kPreTiles : 2;  // LDS stages
+  constexpr int NSLOT = PRE ? kPreTiles : 1; // register sets of staged tiles
 
   // Yat with d_k <= 32 forms its key norms here, from the K fragments its
   // score MFMAs read anyway: the same instruction, k-step order and start
@@ -601,10 +606,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // and wave instead of a pre-pass launch, which costs more at these widths.
   constexpr bool NK_LOCAL = yat_local_norms(VAR, DK);
 
-  // Two LDS stages: the tile being computed and the next one being filled.
-  __shared__ __attribute__((aligned(16))) unsigned short sK[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sV[2][DVP * VLD];
-  __shared__ __attribute__((aligned(16))) float sNK[2][BN];
+  // Two LDS stages (the tile being computed and the next one being filled),
+  // or one per tile with PRE.
+  __shared__ __attribute__((aligned(16))) unsigned short sK[NSTG][BN * KLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[NSTG][DVP * VLD];
+  __shared__ __attribute__((aligned(16))) float sNK[NSTG][BN];
   __shared__ __attribute__((aligned(16))) float sNKw[NK_LOCAL ? NW : 1][NK_LOCAL ? BN : 4];
   __shared__ float sNQ[BM];
 
@@ -666,15 +672,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const int t_begin = min(split * tps, n_tiles);
   const int t_end = min(t_begin + tps, n_tiles);
 
-  // Staging registers for the next key/value tile.
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[V_PER_T][4];
-  f32x4 nkreg = {0.f, 0.f, 0.f, 0.f};
+  // Staging registers for the next key/value tile (PRE: for every tile).
+  u32x4 kreg[NSLOT][K_PER_T];
+  u32x4 vreg[NSLOT][V_PER_T][4];
+  f32x4 nkreg[NSLOT];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) nkreg[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A tile wholly inside T_k takes plain offsets (one add per load); the
   // last, partial tile points its rows >= T_k past the slice (loads give 0).
+  // `slot` (a compile-time index) names the register set.
   static_assert(NT % KCH == 0 && NT % (BN / 4) == 0, "load offsets step evenly");
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](int k0, auto slot) {
+    constexpr int SL = decltype(slot)::value;
     const bool full = k0 + BN <= p.Tk;
     const uint32_t koff = (uint32_t)(((k0 + tid / KCH) * kst + 8 * (tid % KCH)) * 2);
     const uint32_t kstep = (uint32_t)((NT / KCH) * kst * 2);
@@ -682,7 +692,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     for (int i = 0; i < K_PER_T; ++i) {
       if (tid + i * NT < K_UNITS) {
         const int row = k0 + (tid + i * NT) / KCH;
-        kreg[i] = ld128(rk, full || row < p.Tk ? koff + i * kstep : k_bytes);
+        kreg[SL][i] = ld128(rk, full || row < p.Tk ? koff + i * kstep : k_bytes);
       }
     }
     const int g4 = tid % (BN / 4);
@@ -694,22 +704,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = k0 + 4 * g4 + r;
-          vreg[i][r] = ld128(rv, full || row < p.Tk ? voff + (uint32_t)(r * vst * 2) : v_bytes);
+          vreg[SL][i][r] = ld128(rv, full || row < p.Tk ? voff + (uint32_t)(r * vst * 2) : v_bytes);
         }
       }
     }
     if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4)
-      nkreg = *(const f32x4*)(nk_slice + k0 + 4 * tid);
+      nkreg[SL] = *(const f32x4*)(nk_slice + k0 + 4 * tid);
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, auto slot) {
+    constexpr int SL = decltype(slot)::value;
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int u = tid + i * NT;
       if (u < K_UNITS) {
         const int j = u / KCH, c = u % KCH;
         const int row = (j & ~31) | k_lds_row(j & 31);
-        *(u32x4*)&sK[buf][row * KLD + 8 * c] = kreg[i];
+        *(u32x4*)&sK[buf][row * KLD + 8 * c] = kreg[SL][i];
       }
     }
 #pragma unroll
@@ -720,8 +731,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         // 4 keys x 8 values -> 8 value rows of 4 keys each.
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const unsigned a0 = vreg[i][0][e], a1 = vreg[i][1][e];
-          const unsigned a2 = vreg[i][2][e], a3 = vreg[i][3][e];
+          const unsigned a0 = vreg[SL][i][0][e], a1 = vreg[SL][i][1][e];
+          const unsigned a2 = vreg[SL][i][2][e], a3 = vreg[SL][i][3][e];
           u32x2 lo, hi;
           lo[0] = lo_halves(a0, a1);
           lo[1] = lo_halves(a2, a3);
@@ -732,14 +743,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         }
       }
     }
-    if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg;
+    if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg[SL];
   };
 
   f32x16 o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
-  float mass = 0.f;       // Yat, s^tau: sum of weights; softmax: sum exp2(x - mref)
-  float mx = -INFINITY;   // Yat: max kappa; s^tau: max s; softmax: max of x = s*log2e/sqrt(dk)
+  float mass = 0.f;       // Yat: sum of weights; s^tau: of weights / (ln 2)^tau; softmax: sum exp2(x - mref)
+  float mx = -INFINITY;   // Yat: max kappa; s^tau: max q.k; softmax: max of x = s*log2e/sqrt(dk)
   float mref = -INFINITY; // softmax: reference maximum of the exponentials
   const float c_sm = scale * kLog2e;
 
@@ -851,29 +862,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           mx = fmaxf(mx, kap);
         }
       }
-    } else {  // s^tau
+    } else {  // s^tau: weights phi^tau / (ln 2)^tau; max_score tracked on q.k
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sacc[kb][r] * scale;
-          // softplus(s) = max(s, 0) + log1p(e), e = exp(-|s|) in (0, 1].  The
-          // rounding error c of u1 = 1 + e is exact (u1 - 1 - e); log1p(e) =
-          // ln(u1) - c/u1 to first order, and c/u1 = c within a relative e.
-          const float e = __builtin_amdgcn_exp2f(-fabsf(s) * kLog2e);
-          const float u1 = 1.f + e;
-          const float c = (u1 - 1.f) - e;
-          const float sp = fmaf(__builtin_amdgcn_logf(u1), kLn2, fmaxf(s, 0.f) - c);
-          float u = __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(sp + 1e-6f));
-          float sm = s;
+          const float x = sacc[kb][r];
+          float u = stau_weight2(x, c_sm, tau);
+          float xm = x;
           if (MASK) {
             const bool ok = allowed(kb, r);
             u = ok ? u : 0.f;
-            sm = ok ? s : -INFINITY;
+            xm = ok ? x : -INFINITY;
           }
           sacc[kb][r] = u;
           mass += u;
-          mx = fmaxf(mx, sm);
+          mx = fmaxf(mx, xm);
         }
     }
 
@@ -901,16 +905,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       }
   };
 
-  // Prologue: the query fragments and the first tile in flight together, one
-  // wait for all of them (none outstanding on entry to the main loop); then
-  // |q|^2 + b, the first tile into its stage, the next into registers.
+  // Prologue: the query fragments and the first tile (PRE: every tile) in
+  // flight together, one wait for all of them (none outstanding on entry to
+  // the main loop); then |q|^2 + b, the first tile into its stage, the next
+  // into registers (PRE: every tile into its own stage).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, (NSLOT > 1 ? 1 : 0)>;
+  using S2 = std::integral_constant<int, (NSLOT > 2 ? 2 : 0)>;
+  using S3 = std::integral_constant<int, (NSLOT > 3 ? 3 : 0)>;
+  static_assert(!PRE || kPreTiles == 4, "the prologue names four slots");
   {
     const uint32_t off = my_q < p.Tq ? (uint32_t)(((int64_t)my_q * p.qs[2] + 8 * half) * 2)
                                      : q_bytes;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
   }
-  if (t_begin < t_end) load_tile(t_begin * BN);
+  if (t_begin < t_end) load_tile(t_begin * BN, S0{});
+  if constexpr (PRE) {
+    if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN, S1{});
+    if (t_begin + 2 < t_end) load_tile((t_begin + 2) * BN, S2{});
+    if (t_begin + 3 < t_end) load_tile((t_begin + 3) * BN, S3{});
+  }
   __builtin_amdgcn_s_waitcnt(0);
   if (is_yat(VAR)) {
     f32x16 g = sinit;
@@ -918,28 +933,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
     if (holds_diag(col, half)) sNQ[32 * w + col] = diag_of(g, col) * kNormScale;
   }
-  if (t_begin < t_end) {
-    store_tile(t_begin & 1);
-    if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN);
+  if constexpr (PRE) {
+    if (t_begin < t_end) store_tile(0, S0{});
+    if (t_begin + 1 < t_end) store_tile(1, S1{});
+    if (t_begin + 2 < t_end) store_tile(2, S2{});
+    if (t_begin + 3 < t_end) store_tile(3, S3{});
+  } else if (t_begin < t_end) {
+    store_tile(t_begin & 1, S0{});
+    if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN, S0{});
   }
   __syncthreads();
   if (is_yat(VAR)) nq = sNQ[32 * w + col];
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int k0 = t * BN, buf = t & 1;
+    const int k0 = t * BN, buf = PRE ? t - t_begin : t & 1;
     // every key of the tile is in this wave's future: nothing to do
     if (!(p.causal && k0 > qw + 31)) {
       const bool need_mask = (p.causal && k0 + BN - 1 > qw) || (k0 + BN > p.Tk);
       if (need_mask) compute(std::true_type{}, buf, k0);
       else compute(std::false_type{}, buf, k0);
     }
-    if (t + 1 < t_end) {
-      // Stage t+1 was last read in iteration t-1, which every wave finished
-      // before the barrier that ended it.
-      store_tile(buf ^ 1);
-      if (t + 2 < t_end) load_tile(k0 + 2 * BN);
+    if constexpr (!PRE) {
+      if (t + 1 < t_end) {
+        // Stage t+1 was last read in iteration t-1, which every wave finished
+        // before the barrier that ended it.
+        store_tile(buf ^ 1, S0{});
+        if (t + 2 < t_end) load_tile(k0 + 2 * BN, S0{});
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // Epilogue: combine the two lanes that share a query, normalise, store.
@@ -947,6 +969,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const float mx_all = pair_max(mx);
   if (p.kv_splits > 1) {
     // partials of this chunk: O (relative to mref for softmax), mass, max, mref
+    // (s^tau: O and mass in units of phi^tau, max as s, like the decode kernel's)
+    const float ounit = VAR == kStau ? stau_unit(tau) : 1.f;
     if (my_q < p.Tq) {
       const int64_t R = (int64_t)p.B * p.Hq * p.Tq;
       const int64_t ri = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
@@ -959,12 +983,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           if (dv0 < DV) {
             f32x4 st;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st[e] = o[d][4 * g4 + e];
+            for (int e = 0; e < 4; ++e) st[e] = VAR == kStau ? o[d][4 * g4 + e] * ounit
+                                                              : o[d][4 * g4 + e];
             *(f32x4*)&po[dv0] = st;
           }
         }
       if (half == 0) {
-        f32x4 st = {mass_all, mx_all, mref, 0.f};
+        f32x4 st = {mass_all * ounit, VAR == kStau ? mx_all * scale : mx_all, mref, 0.f};
         *(f32x4*)&p.part[(int64_t)p.kv_splits * R * p.dv + ((int64_t)split * R + ri) * 4] = st;
       }
     }
@@ -994,8 +1019,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       }
     if (half == 0) {
       const int64_t ri = ((int64_t)b * p.Hq + h) * p.Tq + my_q;
-      if (p.mass) p.mass[ri] = mass_all;
-      if (p.max_score) p.max_score[ri] = VAR == kSoftmax ? mx_all * kLn2 : mx_all;
+      if (p.mass) p.mass[ri] = VAR == kStau ? mass_all * stau_unit(tau) : mass_all;
+      if (p.max_score)
+        p.max_score[ri] = VAR == kSoftmax ? mx_all * kLn2 : VAR == kStau ? mx_all * scale : mx_all;
     }
   }
 }
@@ -1005,6 +1031,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #ifndef SFS_BN
 #define SFS_BN 64
 #endif
+
+// the instantiations with PRE (others compile it as false)
+template <int VAR, int DK, int DV>
+constexpr bool kPreBuilt = VAR == kSoftmax && DK <= 64 && DV <= 64;
 
 template <int VAR, int DV>
 hipError_t launch_variant(const Problem& p, hipStream_t stream) {
@@ -1017,14 +1047,28 @@ hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   // p.block_rows and p.kv_splits come from the host plan (make_plan)
   const unsigned bh = (unsigned)p.B * (unsigned)p.Hq;
   const unsigned nq = (unsigned)((p.Tq + p.block_rows - 1) / p.block_rows) * bh;
+  // short key ranges (every workgroup at most kPreTiles tiles) preload all
+  // of their tiles with the softmax map; kept to d <= 64, where the staging
+  // registers fit
+  const int tile_keys = p.block_rows == 128 ? 64 : 32;
+  const bool pre = VAR == kSoftmax && DK <= 64 && DV <= 64 && p.kv_splits == 1 &&
+                   p.Tk <= kPreTiles * tile_keys;
   if (p.block_rows == 256) {
     hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(nq), dim3(512), 0, stream, p);
   } else if (p.block_rows == 128) {
-    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64>), dim3(nq, p.kv_splits),
-                       dim3(256), 0, stream, p);
+    if (pre)
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, kPreBuilt<VAR, DK, DV>>),
+                         dim3(nq, p.kv_splits), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, false>), dim3(nq, p.kv_splits),
+                         dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32>), dim3(nq, p.kv_splits),
-                       dim3(128), 0, stream, p);
+    if (pre)
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32, kPreBuilt<VAR, DK, DV>>),
+                         dim3(nq, p.kv_splits), dim3(128), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32, false>), dim3(nq, p.kv_splits),
+                         dim3(128), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -52,6 +52,32 @@ __device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps) {
   return fmaf(y, 0x1p96f, eps);
 }
 
+// s^tau ("s^tau" forum post, core formula): phi = softplus(s) + 1e-6 and the
+// weight phi^tau, here in base-2 units.  With y = s log2(e) + c0 (c0 the floor
+// 1e-6 in the same units),
+//   Z = phi / ln 2 = max(y, c0) + log2(1 + 2^-|y|),
+// which moves the floor into the fma that forms y (2^-|y| then differs from
+// 2^-|s log2 e| by a relative 1e-6 at most).  log2(1 + e) is log2 of
+// u1 = 1 + e plus the rounding error of u1, e - (u1 - 1), times log2(e) (to
+// first order; the factor 1/u1 it drops changes it by a relative e, and it is
+// below 2^-23 itself), so small e keep their relative precision.  The
+// weight returned is Z^tau = phi^tau / (ln 2)^tau: the constant factor of a
+// head cancels in the normalised output; stau_unit gives it for the mass.
+// x: the raw score q.k; c1 = log2(e) / sqrt(d_k).
+constexpr float kStauFloor2 = 1e-6f * kLog2e;
+__device__ __forceinline__ float stau_weight2(float x, float c1, float tau) {
+  const float y = fmaf(x, c1, kStauFloor2);
+  const float e = __builtin_amdgcn_exp2f(-fabsf(y));
+  const float u1 = 1.f + e;
+  const float r = e - (u1 - 1.f);
+  const float z = fmaf(r, kLog2e, fmaxf(y, kStauFloor2)) + __builtin_amdgcn_logf(u1);
+  return __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(z));
+}
+// (ln 2)^tau: stau_weight2 times this is phi^tau
+__device__ __forceinline__ float stau_unit(float tau) {
+  return exp2f(tau * -0.52876637294031f);  // log2(ln 2)
+}
+
 // acc + the two bf16 halves of x, in fp32, one instruction (v_dot2 with ones)
 __device__ __forceinline__ float add_bf16_pair(unsigned x, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};

@@ -77,6 +77,26 @@ def test_medium_shapes_bf16(variant, shape):
     full_check(inp, variant, causal, "medium", BLOCK_ROWS)
 
 
+# Short key ranges: the small-grid kernels preload every tile (at most 4 per
+# workgroup: T_k <= 256 for 128-row and <= 128 for 64-row workgroups, d <= 64)
+PRELOAD = [
+    (2, 4, 2, 256, 256, 32, 32, True),    # 4 full tiles (128 rows)
+    (2, 2, 1, 100, 128, 64, 64, False),   # 4 full 32-key tiles (64 rows), 2 (128 rows)
+    (1, 4, 2, 300, 60, 16, 32, False),    # one ragged tile, T_q > T_k
+    (3, 2, 2, 33, 33, 64, 16, True),      # one tile, one query tile
+    (1, 2, 2, 190, 190, 32, 64, True),    # ragged third tile
+    (1, 2, 2, 129, 257, 64, 64, False),   # one key past the preload range
+]
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", PRELOAD, ids=lambda s: "x".join(map(str, s)))
+def test_short_key_ranges_bf16(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=28, qk_std=1.5)
+    full_check(inp, variant, causal, "preload", BLOCK_ROWS)
+
+
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
 @pytest.mark.parametrize("shape", [(1, 2, 1, 100, 100, 32, 64, True),
                                    (2, 2, 2, 33, 90, 128, 16, False)],
