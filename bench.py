@@ -107,9 +107,10 @@ def bwd_flops(wl) -> float:
     return float(wl.allowed_pairs) * 2.0 * (3 * wl.dk + 2 * wl.dv)
 
 
-def time_calls(fn, stream, steps, warmup):
+def time_calls(fn, stream, steps, warmup, per_call=None):
     """Average per-call duration (ms) by HIP events on `stream`, plus the
-    wall time of the whole timed region."""
+    wall time of the whole timed region.  `per_call`, a list, receives every
+    call's duration."""
     import torch
     for _ in range(warmup):
         fn()
@@ -124,7 +125,64 @@ def time_calls(fn, stream, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if per_call is not None:
+        per_call.extend(per)
     return float(np.mean(per)), float(np.median(per)), wall
+
+
+def spread(per):
+    """Spread of the per-call durations of the timed region (ms)."""
+    a = np.asarray(per, dtype=np.float64)
+    return {"min_ms": round(float(a.min()), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "median_ms": round(float(np.median(a)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "max_ms": round(float(a.max()), 4),
+            "cv": round(float(a.std() / a.mean()), 4)}
+
+
+def engine_clock(fn, warm=1.0, readings_n=3, gap=0.25):
+    """The GFX engine clock under this load: the timed call is enqueued in a
+    loop by a second thread (after the timed region); after `warm` seconds of
+    it, `amd-smi metric --clock` is read `readings_n` times, `gap` apart.
+    Returns the mean clock over the XCDs of each reading (MHz) and their
+    median, or None where amd-smi is missing or its output does not parse."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi")
+    if not exe:
+        return None
+    stop = threading.Event()
+
+    def load():
+        while not stop.is_set():
+            fn()
+
+    th = threading.Thread(target=load, daemon=True)
+    th.start()
+    readings = []
+    try:
+        time.sleep(warm)
+        for _ in range(readings_n):
+            try:
+                out = subprocess.run([exe, "metric", "-g", "0", "--clock"], capture_output=True,
+                                     text=True, timeout=20).stdout
+            except (OSError, subprocess.SubprocessError):
+                continue
+            clk = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+            if clk:
+                readings.append(round(float(np.mean(clk)), 1))
+            time.sleep(gap)
+    finally:
+        stop.set()
+        th.join()
+        torch.cuda.synchronize()
+    if not readings:
+        return None
+    return {"gfx_mhz_mean_over_xcds": readings, "median_mhz": float(np.median(readings)),
+            "source": f"amd-smi metric --clock, read {len(readings)} times while the timed "
+                      f"call ran in a loop (after {warm:.1f} s of it, following the timed region)"}
 
 
 def cpu_baseline(inp, variant, target_s=25.0):
@@ -168,6 +226,8 @@ def main():
     ap.add_argument("--workload", default="long_yat")
     ap.add_argument("--variant", default="yat")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the engine-clock reading after the timed region")
     ap.add_argument("--rotate-mib", type=int, default=0,
                     help="cycle over enough distinct copies of the inputs and outputs to "
                          "span this many MiB (larger than the 256 MB Infinity Cache, so "
@@ -232,7 +292,8 @@ def main():
     flops = alg_flops(wl)
     primary = args.variant
     torch.cuda.synchronize()
-    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup)
+    per_call = []
+    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup, per_call)
     others = {}
     for var in wl.variants:
         if var != primary:
@@ -262,6 +323,8 @@ def main():
                    "kv_splits": args.kv_splits,
                    "parallelism": "none (1 GPU)"},
         "roofline": {**roof,
+                     "scope": "step: the whole call, every kernel it launches, event-timed "
+                              "(kernel-level figures from the trace are in profiles/)",
                      "traffic": recorded_traffic(wl.name, primary, uses_decode_kernel(wl, args)),
                      "traffic_unit": "bytes per launch of "
                                      f"{'attn_decode_bf16' if uses_decode_kernel(wl, args) else 'attn_fwd_bf16'}"
@@ -273,12 +336,15 @@ def main():
                      "arithmetic_intensity_flop_per_byte": round(ai, 1)},
         "alg_bytes_gbs": round(alg_bytes(wl) / (mean_ms * 1e-3) / 1e9, 1),
         "wall_s_timed_region": round(wall, 3),
+        "spread": spread(per_call),
     }
     for var, r in others.items():
         line[var] = {k2: round(v2, 4) for k2, v2 in r.items()}
     if "softmax" in others:
         # > 1 means the primary branch is faster than softmax on the same inputs
         line[f"{primary}_speed_vs_softmax"] = round(others["softmax"]["ms"] / mean_ms, 4)
+    if not args.no_clock:
+        line["engine_clock"] = engine_clock(call(primary))
     line["roofline"]["alg_bytes_per_launch"] = alg_bytes(wl)
     line["kernel_source_sha256_16"] = kernel_source_hash(uses_decode_kernel(wl, args))
     if args.copy_calibration_mib:
@@ -358,7 +424,8 @@ def bench_backward(args, wl, inp):
     flops = bwd_flops(wl)
     primary = args.variant
     torch.cuda.synchronize()
-    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup)
+    per_call = []
+    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup, per_call)
     others = {}
     for var in wl.variants:
         if var != primary:
@@ -383,8 +450,10 @@ def bench_backward(args, wl, inp):
                      "kernel": f"attn_bwd ({primary}): row prep, D pass, dK/dV and dQ kernels; "
                                f"flops = {flops:.4e} per call ({wl.allowed_pairs} allowed "
                                f"pairs x 2(3 dk + 2 dv))",
-                     "median_ms": round(med_ms, 4)},
+                     "median_ms": round(med_ms, 4),
+                     "scope": "step: the whole attn_bwd call, every kernel it launches"},
         "wall_s_timed_region": round(wall, 3),
+        "spread": spread(per_call),
     }
     for var, r in others.items():
         line[var] = {k2: round(v2, 4) for k2, v2 in r.items()}
