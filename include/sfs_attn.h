@@ -172,6 +172,8 @@ int attn_fwd(const attn_desc* desc, const void* q, const void* k, const void* v,
  * (nothing enqueued).  Every call on one GPU shares that GPU's scratch, which
  * keeps the last call's contents (no call relies on them): calls that may
  * run concurrently on one GPU (different streams) race, so order them.
+ * The first call on a GPU looks up the scratch's device address; make it
+ * before capturing a graph, whose replays then re-run the captured kernels.
  * Results are identical to attn_fwd's on the same inputs. */
 #define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
 int attn_fwd_noalloc(const attn_desc* desc, const void* q, const void* k, const void* v,

@@ -95,3 +95,42 @@ def test_noalloc_torch_binding_matches():
     torch.cuda.synchronize()
     _same(ref, got, "torch binding")
 
+
+
+@pytest.mark.parametrize("case", ["yat_prefill", "stau_keysplit"])
+def test_noalloc_in_a_captured_graph(case):
+    # the caller the entry point is for: the call captured once into a HIP
+    # graph on fixed buffers, then replayed on new inputs copied into them;
+    # every replay must equal an eager attn_fwd on the same inputs
+    shape, variant, causal, rows, splits = CASES[case][1]
+    inputs = [make_custom(*shape, causal=causal, seed=40 + i) for i in range(3)]
+    bufs = [t.clone() for t in to_device(inputs[0])[:3]]
+    prm = to_device(inputs[0])[3]
+    B, Hq, Tq, _ = bufs[0].shape
+    out = torch.empty(B, Hq, Tq, bufs[2].shape[3], dtype=bufs[0].dtype, device=bufs[0].device)
+    mass = torch.empty(B, Hq, Tq, dtype=torch.float32, device=out.device)
+    mx = torch.empty_like(mass)
+    kw = dict(causal=causal, block_rows=rows, kv_splits=splits, out=out, mass=mass, max_score=mx,
+              **prm)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        attn.attn_fwd_noalloc(*bufs, variant, stream=side.cuda_stream, **kw)  # first call: set-up
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            attn.attn_fwd_noalloc(*bufs, variant, stream=side.cuda_stream, **kw)
+    torch.cuda.synchronize()
+    for i, inp in enumerate(inputs):
+        say(f"noalloc graph {case}: replay {i}")
+        q, k, v, _ = to_device(inp)
+        for dst, src in zip(bufs, (q, k, v)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = attn.attn_fwd(q, k, v, variant, causal=causal, block_rows=rows, kv_splits=splits,
+                            **prm)
+        torch.cuda.synchronize()
+        _same(ref, (out, mass, mx), f"{case} replay {i}")
