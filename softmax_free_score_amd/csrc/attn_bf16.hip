@@ -308,7 +308,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   float mass = 0.f;         // Yat: sum of weights; s^tau: of weights / (ln 2)^tau; softmax: sum exp2(x - mref)
   float mx = -INFINITY;     // Yat: max kappa; s^tau: max q.k; softmax: max of x = s*log2e/sqrt(dk)
   float mref = -INFINITY;   // softmax: reference maximum of the exponentials
-  const float c_sm = scale * kLog2e;
+  const MapConsts mc = map_consts(scale * kLog2e);
+  const float c_sm = mc.c_sm;
 
   // wave has work on tile t unless all its keys lie in the wave's future
   auto active = [&](int t) { return !(p.causal && t * BN > qw + 31); };
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
           float den[8], rc[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r)
-            den[r] = yat_den(sacc[kb][r0 + r], nq + nk[r0 + r], eps);
+            den[r] = yat_den(sacc[kb][r0 + r], nq + nk[r0 + r], eps, mc);
 #pragma unroll
           for (int r = 0; r < 8; ++r) rc[r] = __builtin_amdgcn_rcpf(den[r]);
 #pragma unroll
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = sacc[kb][r];
-          float u = stau_weight2(x, c_sm, tau);
+          float u = stau_weight2(x, tau, mc);
           float xm = x;
           if (MASK) {
             const bool ok = allowed(kb, r);
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
         // Yat's mass is the sum of the bf16 weights the value MFMA takes
         if (is_yat(VAR)) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass);
+          for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass, mc);
         }
         pb[kb][s] = __builtin_bit_cast(bf16x8, pw);
       }
@@ -752,7 +753,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   float mass = 0.f;       // Yat: sum of weights; s^tau: of weights / (ln 2)^tau; softmax: sum exp2(x - mref)
   float mx = -INFINITY;   // Yat: max kappa; s^tau: max q.k; softmax: max of x = s*log2e/sqrt(dk)
   float mref = -INFINITY; // softmax: reference maximum of the exponentials
-  const float c_sm = scale * kLog2e;
+  const MapConsts mc = map_consts(scale * kLog2e);
+  const float c_sm = mc.c_sm;
 
   // One tile of BN keys against the wave's 32 queries.
   auto compute = [&](auto mask_tag, int buf, int k0) {
@@ -856,7 +858,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         for (int r = 0; r < 16; ++r) {
           const float u = sacc[kb][r];  // q.k + b
           float kap = yat_numerator<VAR>(u, p.yat_power) *
-                      __builtin_amdgcn_rcpf(yat_den(u, nq + nk[r], eps));
+                      __builtin_amdgcn_rcpf(yat_den(u, nq + nk[r], eps, mc));
           if (MASK) kap = allowed(kb, r) ? kap : 0.f;
           sacc[kb][r] = kap;
           mx = fmaxf(mx, kap);
@@ -868,7 +870,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = sacc[kb][r];
-          float u = stau_weight2(x, c_sm, tau);
+          float u = stau_weight2(x, tau, mc);
           float xm = x;
           if (MASK) {
             const bool ok = allowed(kb, r);
@@ -893,7 +895,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         // Yat's mass is the sum of the bf16 weights the value MFMA takes
         if (is_yat(VAR)) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass);
+          for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass, mc);
         }
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll

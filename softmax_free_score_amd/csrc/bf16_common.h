@@ -52,6 +52,31 @@ __device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps) {
   return fmaf(y, 0x1p96f, eps);
 }
 
+// Map constants held in scalar registers.  -2 kNormScale, 2^96, log2(e), the
+// s^tau floor and the score scale are not inline constants, so an instruction
+// would otherwise carry each as a 32-bit literal, which halves its issue rate;
+// a scalar register operand costs nothing (one per instruction).
+struct MapConsts {
+  float m2s;    // -2 kNormScale
+  float k96;    // 2^96
+  float l2e;    // log2(e)
+  float floor2; // kStauFloor2
+  float c_sm;   // log2(e) / sqrt(d_k)
+  unsigned ones;  // the bf16 pair (1, 1)
+};
+__device__ __forceinline__ MapConsts map_consts(float c_sm) {
+  MapConsts c{-2.f * kNormScale, 0x1p96f, kLog2e, 1e-6f * kLog2e, c_sm, 0x3f803f80u};
+  // opaque to constant folding: the values stay in scalar registers
+  asm volatile("" : "+s"(c.m2s), "+s"(c.k96), "+s"(c.l2e), "+s"(c.floor2), "+s"(c.c_sm),
+               "+s"(c.ones));
+  return c;
+}
+__device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps,
+                                         const MapConsts& mc) {
+  const float y = __builtin_amdgcn_fmed3f(fmaf(u, mc.m2s, nqk_scaled), 0.f, 1.f);
+  return fmaf(y, mc.k96, eps);
+}
+
 // s^tau ("s^tau" forum post, core formula): phi = softplus(s) + 1e-6 and the
 // weight phi^tau, here in base-2 units.  With y = s log2(e) + c0 (c0 the floor
 // 1e-6 in the same units),
@@ -73,6 +98,15 @@ __device__ __forceinline__ float stau_weight2(float x, float c1, float tau) {
   const float z = fmaf(r, kLog2e, fmaxf(y, kStauFloor2)) + __builtin_amdgcn_logf(u1);
   return __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(z));
 }
+// The same with the constants from scalar registers (c1 = mc.c_sm).
+__device__ __forceinline__ float stau_weight2(float x, float tau, const MapConsts& mc) {
+  const float y = fmaf(x, mc.c_sm, mc.floor2);
+  const float e = __builtin_amdgcn_exp2f(-fabsf(y));
+  const float u1 = 1.f + e;
+  const float r = e - (u1 - 1.f);
+  const float z = fmaf(r, mc.l2e, fmaxf(y, mc.floor2)) + __builtin_amdgcn_logf(u1);
+  return __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(z));
+}
 // (ln 2)^tau: stau_weight2 times this is phi^tau
 __device__ __forceinline__ float stau_unit(float tau) {
   return exp2f(tau * -0.52876637294031f);  // log2(ln 2)
@@ -82,6 +116,11 @@ __device__ __forceinline__ float stau_unit(float tau) {
 __device__ __forceinline__ float add_bf16_pair(unsigned x, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), ones, acc, false);
+}
+// The same with the pair of ones from a scalar register.
+__device__ __forceinline__ float add_bf16_pair(unsigned x, float acc, const MapConsts& mc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                         __builtin_bit_cast(bf16x2, mc.ones), acc, false);
 }
 // Two bf16 words from two packed pairs, one byte permute each: the low
 // halves of a and b (a's in the low half of the result), or the high halves.
