@@ -260,10 +260,11 @@ int attn_telemetry(const attn_desc* desc, const void* q, const void* k, int vari
  * q, k, v        the forward's inputs, device bf16, strides of desc.
  * dout           device bf16 [B,Hq,Tq,dv], strides desc->o_stride.
  * mass,          the forward's row statistics, device fp32 [B,Hq,Tq],
- * max_score      contiguous: mass for ATTN_SOFTMAX and ATTN_STAU, max_score
- *                for ATTN_SOFTMAX.  ATTN_YAT reads neither (may be NULL): it
- *                forms mass + 1e-9 again from the kappa it differentiates,
- *                so that the weights and their normaliser round alike.
+ * max_score      contiguous, read for ATTN_SOFTMAX only.  ATTN_YAT and
+ *                ATTN_STAU read neither (may be NULL): they form the row
+ *                normaliser again (Yat mass + 1e-9, s^tau mass) from the
+ *                weights they differentiate, so that the weights and their
+ *                normaliser round alike.
  * dq, dk, dv     device bf16 outputs laid out like q, k and v (q_stride,
  *                k_stride, v_stride); every element is written (dk = dv = 0
  *                when T_q == 0).  They must not alias any input.

@@ -408,8 +408,8 @@ def attn_bwd(q, k, v, dout, variant, mass, max_score=None, b_raw=None, eps_raw=N
     with dq, dk, dv (bf16, laid out like q, k, v) and, when ``param_grads``,
     the per-head parameter gradients of the variant (db_raw and deps_raw for
     Yat, dlog_tau for s^tau; float32 [Hq]).  ``mass`` and ``max_score`` are
-    the forward's row statistics (softmax needs both, s^tau the mass; Yat
-    reads neither and takes None); ``dout`` is dL/dout [B, Hq, Tq, dv]."""
+    the forward's row statistics (softmax needs both; Yat and s^tau read
+    neither and take None); ``dout`` is dL/dout [B, Hq, Tq, dv]."""
     variant = VARIANTS.get(variant, variant)
     _check_qkv(q, k, v)
     B, Hq, Tq, _ = q.shape

@@ -461,10 +461,9 @@ int attn_bwd(const attn_desc* d, const void* q, const void* k, const void* v,
                     workspace, workspace_bytes, false, &empty, need);
   if (st != ATTN_OK) return st;
   if (!empty) {
-    if (!dq || !dk || !dv || (variant != ATTN_YAT && !mass) ||
-        (variant == ATTN_SOFTMAX && !max_score)) {
-      set_error("the backward needs dq, dk, dv, the forward's mass (softmax, s^tau) and, "
-                "for softmax, its max_score");
+    if (!dq || !dk || !dv || (variant == ATTN_SOFTMAX && (!mass || !max_score))) {
+      set_error("the backward needs dq, dk, dv and, for softmax, the forward's mass and "
+                "max_score");
       return ATTN_ERR_NULL;
     }
     if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) {

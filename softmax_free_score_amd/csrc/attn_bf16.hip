@@ -309,6 +309,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   float mx = -INFINITY;     // Yat: max kappa; s^tau: max q.k; softmax: max of x = s*log2e/sqrt(dk)
   float mref = -INFINITY;   // softmax: reference maximum of the exponentials
   const MapConsts mc = map_consts(scale * kLog2e);
+  const StauPoly sp = stau_poly();
   const float c_sm = mc.c_sm;
 
   // wave has work on tile t unless all its keys lie in the wave's future
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = sacc[kb][r];
-          float u = stau_weight2(x, tau, mc);
+          float u = stau_weight2(x, tau, mc, sp);
           float xm = x;
           if (MASK) {
             const bool ok = allowed(kb, r);
@@ -754,6 +755,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   float mx = -INFINITY;   // Yat: max kappa; s^tau: max q.k; softmax: max of x = s*log2e/sqrt(dk)
   float mref = -INFINITY; // softmax: reference maximum of the exponentials
   const MapConsts mc = map_consts(scale * kLog2e);
+  const StauPoly sp = stau_poly();
   const float c_sm = mc.c_sm;
 
   // One tile of BN keys against the wave's 32 queries.
@@ -870,7 +872,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = sacc[kb][r];
-          float u = stau_weight2(x, tau, mc);
+          float u = stau_weight2(x, tau, mc, sp);
           float xm = x;
           if (MASK) {
             const bool ok = allowed(kb, r);

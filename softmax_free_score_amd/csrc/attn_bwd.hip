@@ -720,8 +720,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
   if (my_q < p.Tq) {
     const int64_t idx = row_idx;
     if (!DELTA) D = p.row_d[idx];
-    // Yat's D pass forms the normaliser itself (below): its weights are kappa
-    Z = DELTA && is_yat(VAR) ? 1.f : p.row_z[idx];
+    // the Yat and s^tau D pass forms the normaliser itself (below): its
+    // weights are then kappa or phi^tau
+    Z = DELTA && VAR != kSoftmax ? 1.f : p.row_z[idx];
     if (is_yat(VAR)) nq = p.nq[idx];
   }
   const HeadC hc = head_consts<VAR, DK>(p, h);
@@ -785,7 +786,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                                // the sum of B'/2 = bf16(g/2) - A/2)
   float sum0 = 0.f, sum1 = 0.f;  // Yat: sum A/2, sum B/2; s^tau: sum w (dp - D) log2(phi)
   float dsum = 0.f;            // DELTA: sum over the lane's keys of w dp (Yat: kappa dp)
-  float msum = 0.f;            // DELTA, Yat: sum over the lane's keys of kappa
+  float msum = 0.f;            // DELTA, Yat, s^tau: sum over the lane's keys of kappa or phi^tau
 
   // Scores of one tile -> packed gradient scores (pg) and the row sums.
   auto scores = [&](auto mask_tag, int buf, int k0, u32x4* pg) {
@@ -828,7 +829,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
           if (DELTA) {
             const float wv = ok ? pair_weight<VAR>(sacc[r], Z, nq + nkv, hc) : 0.f;
             dsum = fmaf(wv, pacc[r], dsum);
-            if (is_yat(VAR)) msum += wv;
+            if (VAR != kSoftmax) msum += wv;
             gv[o] = av[o] = lv[o] = 0.f;
           } else {
             pair_grad<VAR>(sacc[r], pacc[r], D, Z, nq + nkv, hc, gv[o], av[o], lv[o]);
@@ -892,6 +893,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
       // dp - D cancels where the exact gradient does (a row whose weight sits
       // on one key), whatever rounding the forward's kappa took
       const float z = 1.f / (pair_sum(msum) + 1e-9f);
+      if (my_q < p.Tq && half == 0) {
+        p.row_z[row_idx] = z;
+        p.row_d[row_idx] = dsum * z;
+      }
+    } else if (VAR == kStau) {
+      // Z = 1 / sum_j phi^tau from these same weights: the forward's mass
+      // carries that kernel's own rounding (it takes log2(1 + t) from a
+      // polynomial), which would otherwise scale every weight here and enter
+      // the parameter sum through dp - D
+      const float m = pair_sum(msum);
+      const float z = m > 0.f ? 1.f / m : 0.f;
       if (my_q < p.Tq && half == 0) {
         p.row_z[row_idx] = z;
         p.row_d[row_idx] = dsum * z;

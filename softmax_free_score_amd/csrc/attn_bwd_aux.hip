@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdProblem p) {
   float z = 0.f;
   if (i < p.Tq) {
     const int64_t ri = bh * p.Tq + i;
+    // (Yat and s^tau: the D pass forms Z from its own weights)
     if (p.variant == kSoftmax) z = fmaf(p.max_score[ri], kLog2eF, log2f(p.mass[ri]));
-    else if (p.variant == kStau) z = p.mass[ri] > 0.f ? 1.f / p.mass[ri] : 0.f;
   }
   p.row_d[r] = 0.f;
   p.row_z[r] = z;

@@ -52,23 +52,23 @@ __device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps) {
   return fmaf(y, 0x1p96f, eps);
 }
 
-// Map constants held in scalar registers.  -2 kNormScale, 2^96, log2(e), the
-// s^tau floor and the score scale are not inline constants, so an instruction
+// Map constants held in scalar registers.  -2 kNormScale, 2^96, the s^tau
+// floor and the score scale are not inline constants, so an instruction
 // would otherwise carry each as a 32-bit literal, which halves its issue rate;
 // a scalar register operand costs nothing (one per instruction).
+// The s^tau floor 1e-6 in base-2 units (see stau_weight2 below).
+constexpr float kStauFloor2 = 1e-6f * kLog2e;
 struct MapConsts {
   float m2s;    // -2 kNormScale
   float k96;    // 2^96
-  float l2e;    // log2(e)
   float floor2; // kStauFloor2
   float c_sm;   // log2(e) / sqrt(d_k)
   unsigned ones;  // the bf16 pair (1, 1)
 };
 __device__ __forceinline__ MapConsts map_consts(float c_sm) {
-  MapConsts c{-2.f * kNormScale, 0x1p96f, kLog2e, 1e-6f * kLog2e, c_sm, 0x3f803f80u};
+  MapConsts c{-2.f * kNormScale, 0x1p96f, kStauFloor2, c_sm, 0x3f803f80u};
   // opaque to constant folding: the values stay in scalar registers
-  asm volatile("" : "+s"(c.m2s), "+s"(c.k96), "+s"(c.l2e), "+s"(c.floor2), "+s"(c.c_sm),
-               "+s"(c.ones));
+  asm volatile("" : "+s"(c.m2s), "+s"(c.k96), "+s"(c.floor2), "+s"(c.c_sm), "+s"(c.ones));
   return c;
 }
 __device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps,
@@ -82,29 +82,35 @@ __device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps,
 // 1e-6 in the same units),
 //   Z = phi / ln 2 = max(y, c0) + log2(1 + 2^-|y|),
 // which moves the floor into the fma that forms y (2^-|y| then differs from
-// 2^-|s log2 e| by a relative 1e-6 at most).  log2(1 + e) is log2 of
-// u1 = 1 + e plus the rounding error of u1, e - (u1 - 1), times log2(e) (to
-// first order; the factor 1/u1 it drops changes it by a relative e, and it is
-// below 2^-23 itself), so small e keep their relative precision.  The
-// weight returned is Z^tau = phi^tau / (ln 2)^tau: the constant factor of a
-// head cancels in the normalised output; stau_unit gives it for the mass.
-// x: the raw score q.k; c1 = log2(e) / sqrt(d_k).
-constexpr float kStauFloor2 = 1e-6f * kLog2e;
-__device__ __forceinline__ float stau_weight2(float x, float c1, float tau) {
-  const float y = fmaf(x, c1, kStauFloor2);
-  const float e = __builtin_amdgcn_exp2f(-fabsf(y));
-  const float u1 = 1.f + e;
-  const float r = e - (u1 - 1.f);
-  const float z = fmaf(r, kLog2e, fmaxf(y, kStauFloor2)) + __builtin_amdgcn_logf(u1);
-  return __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(z));
+// 2^-|s log2 e| by a relative 1e-6 at most).  With t = 2^-|y| in (0, 1],
+// log2(1 + t) = t P(t), P a degree-5 polynomial for log2(1 + t) / t on [0, 1]
+// that is minimax in relative error (Lawson's algorithm; the fit is
+// softmax_free_score_amd/stau_poly.py): relative error below 8.6e-6 with fp32
+// Horner, and t P(t) keeps that relative precision for small t, where
+// Z ~ c0 + t / ln 2.  The weight returned is Z^tau = phi^tau / (ln 2)^tau: the
+// constant factor of a head cancels in the normalised output; stau_unit gives
+// it for the mass.  Three transcendentals: exp2, log2, exp2.
+struct StauPoly {
+  float c0, c1, c2, c3, c4, c5;
+};
+__device__ __forceinline__ StauPoly stau_poly() {
+  StauPoly s{1.4426828622817993f, -0.7204261422157288f, 0.4691740572452545f,
+             -0.3030361831188202f, 0.14603286981582642f, -0.03443589806556702f};
+  // scalar registers rather than 32-bit literals, as MapConsts above
+  asm("" : "+s"(s.c0), "+s"(s.c1), "+s"(s.c2), "+s"(s.c3), "+s"(s.c4), "+s"(s.c5));
+  return s;
 }
-// The same with the constants from scalar registers (c1 = mc.c_sm).
-__device__ __forceinline__ float stau_weight2(float x, float tau, const MapConsts& mc) {
+// x: the raw score q.k; mc.c_sm = log2(e) / sqrt(d_k).
+__device__ __forceinline__ float stau_weight2(float x, float tau, const MapConsts& mc,
+                                             const StauPoly& sp) {
   const float y = fmaf(x, mc.c_sm, mc.floor2);
-  const float e = __builtin_amdgcn_exp2f(-fabsf(y));
-  const float u1 = 1.f + e;
-  const float r = e - (u1 - 1.f);
-  const float z = fmaf(r, mc.l2e, fmaxf(y, mc.floor2)) + __builtin_amdgcn_logf(u1);
+  const float t = __builtin_amdgcn_exp2f(-fabsf(y));
+  float l = fmaf(sp.c5, t, sp.c4);
+  l = fmaf(l, t, sp.c3);
+  l = fmaf(l, t, sp.c2);
+  l = fmaf(l, t, sp.c1);
+  l = fmaf(l, t, sp.c0);
+  const float z = fmaf(l, t, fmaxf(y, mc.floor2));
   return __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(z));
 }
 // (ln 2)^tau: stau_weight2 times this is phi^tau

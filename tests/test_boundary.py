@@ -302,7 +302,7 @@ def test_bwd_validation():
     assert call_bwd(desc(), mx=0) == ERR_NULL                        # softmax needs max_score
     assert call_bwd(desc(), variant=attn.ATTN_YAT, mx=0) == ERR_HIP  # Yat does not
     assert call_bwd(desc(), variant=attn.ATTN_YAT, mass=0, mx=0) == ERR_HIP  # nor the mass
-    assert call_bwd(desc(), variant=attn.ATTN_STAU, mass=0) == ERR_NULL
+    assert call_bwd(desc(), variant=attn.ATTN_STAU, mass=0, mx=0) == ERR_HIP  # s^tau neither
     assert call_bwd(desc(), variant=attn.ATTN_YAT, b=0) == ERR_PARAM
     assert call_bwd(desc(), variant=attn.ATTN_STAU, lt=0) == ERR_PARAM
     # parameter gradients are optional
