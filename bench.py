@@ -107,11 +107,30 @@ def bwd_flops(wl) -> float:
     return float(wl.allowed_pairs) * 2.0 * (3 * wl.dk + 2 * wl.dv)
 
 
-def time_calls(fn, stream, steps, warmup, per_call=None):
+def settle(fn, ms):
+    """Run `fn` untimed for about `ms` milliseconds of wall time and wait for
+    it: the GPU leaves the idle power state it sat in while the inputs were
+    generated on the host, so the warm-up and timed calls that follow run at
+    the engine clock this load holds (a handful of warm-up calls, a few
+    milliseconds, is shorter than that ramp)."""
+    import torch
+    if ms <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
+def time_calls(fn, stream, steps, warmup, per_call=None, settle_ms=0):
     """Average per-call duration (ms) by HIP events on `stream`, plus the
     wall time of the whole timed region.  `per_call`, a list, receives every
-    call's duration."""
+    call's duration.  `settle_ms`: untimed calls before the warm-up (settle)."""
     import torch
+    settle(fn, settle_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -225,6 +244,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_yat")
     ap.add_argument("--variant", default="yat")
+    ap.add_argument("--settle-ms", type=int, default=300,
+                    help="before each branch's warm-up, run its call untimed for this many "
+                         "milliseconds so that the engine clock has left the idle state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the engine-clock reading after the timed region")
@@ -293,11 +315,13 @@ def main():
     primary = args.variant
     torch.cuda.synchronize()
     per_call = []
-    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup, per_call)
+    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup, per_call,
+                                       settle_ms=args.settle_ms)
     others = {}
     for var in wl.variants:
         if var != primary:
-            m2, md2, _ = time_calls(call(var), stream, args.steps, args.warmup)
+            m2, md2, _ = time_calls(call(var), stream, args.steps, args.warmup,
+                                    settle_ms=args.settle_ms)
             others[var] = {"ms": m2, "tflops": flops / (m2 * 1e-3) / 1e12,
                            "frac_bf16_peak": flops / (m2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     value = flops / (mean_ms * 1e-3) / 1e12
@@ -336,6 +360,7 @@ def main():
                      "arithmetic_intensity_flop_per_byte": round(ai, 1)},
         "alg_bytes_gbs": round(alg_bytes(wl) / (mean_ms * 1e-3) / 1e9, 1),
         "wall_s_timed_region": round(wall, 3),
+        "settle_ms_per_branch": args.settle_ms,
         "spread": spread(per_call),
     }
     for var, r in others.items():
@@ -425,11 +450,13 @@ def bench_backward(args, wl, inp):
     primary = args.variant
     torch.cuda.synchronize()
     per_call = []
-    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup, per_call)
+    mean_ms, med_ms, wall = time_calls(call(primary), stream, args.steps, args.warmup, per_call,
+                                       settle_ms=args.settle_ms)
     others = {}
     for var in wl.variants:
         if var != primary:
-            m2, _, _ = time_calls(call(var), stream, args.steps, args.warmup)
+            m2, _, _ = time_calls(call(var), stream, args.steps, args.warmup,
+                                    settle_ms=args.settle_ms)
             others[var] = {"ms": m2, "tflops": flops / (m2 * 1e-3) / 1e12,
                            "frac_bf16_peak": flops / (m2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     value = flops / (mean_ms * 1e-3) / 1e12
@@ -453,6 +480,7 @@ def bench_backward(args, wl, inp):
                      "median_ms": round(med_ms, 4),
                      "scope": "step: the whole attn_bwd call, every kernel it launches"},
         "wall_s_timed_region": round(wall, 3),
+        "settle_ms_per_branch": args.settle_ms,
         "spread": spread(per_call),
     }
     for var, r in others.items():
