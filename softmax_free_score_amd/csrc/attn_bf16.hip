@@ -111,11 +111,15 @@ __global__ __launch_bounds__(256) void yat_key_norms_bf16(Problem p) {
   const uint32_t bytes = slice_bytes(p.Tk, p.ks[2], DK);
   const rsrc_t r = make_rsrc(base, bytes);
   const uint32_t off = row < p.Tk ? (uint32_t)(((int64_t)row * p.ks[2] + 8 * half) * 2) : bytes;
+  // the row's loads are issued before b is formed, so that the parameter
+  // load and softplus run under them
+  u32x4 x[DK / 16];
+#pragma unroll
+  for (int s = 0; s < DK / 16; ++s) x[s] = ld128(r, off + 32 * s);
   f32x16 g = score_init<kYat>(yat_bias(p, h));
 #pragma unroll
   for (int s = 0; s < DK / 16; ++s)
-    g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
-               __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
+    g = mfma32(__builtin_bit_cast(bf16x8, x[s]), __builtin_bit_cast(bf16x8, x[s]), g);
   if (row < p.Tk && holds_diag(col, half))
     p.nk[((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) + row] = diag_of(g, col) * kNormScale;
 }
@@ -193,14 +197,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   const rsrc_t rv = make_rsrc(vbase, v_bytes);
   const int kst = (int)p.ks[2], vst = (int)p.vs[2];
 
-  // Per-head scalars (prologue).
+  // Per-head scalars, formed in the prologue once its loads are in flight.
   float bias = 0.f, eps = 0.f, tau = 0.f;
-  if (is_yat(VAR)) {
-    bias = yat_bias(p, h);
-    eps = softplus_precise(p.eps_raw[h]);
-  } else if (VAR == kStau) {
-    tau = softplus_precise(p.log_tau[h]) + 1.f;
-  }
+  auto head_scalars = [&]() {
+    if (is_yat(VAR)) {
+      bias = yat_bias(p, h);
+      eps = softplus_precise(p.eps_raw[h]);
+    } else if (VAR == kStau) {
+      tau = softplus_precise(p.log_tau[h]) + 1.f;
+    }
+  };
   const float scale = 1.0f / sqrtf((float)DK);
 
   // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7]
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
       is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;
-  const f32x16 sinit = score_init<VAR>(bias);
+  f32x16 sinit = {};  // score_init<VAR>(bias), set in the prologue
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
@@ -492,6 +498,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
   }
   if (grp == 0) load_k(0);
   else load_v(0);
+  head_scalars();
+  sinit = score_init<VAR>(bias);
   __builtin_amdgcn_s_waitcnt(0);
   if (is_yat(VAR)) {
     f32x16 g = sinit;
@@ -644,14 +652,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const rsrc_t rv = make_rsrc(vbase, v_bytes);
   const int kst = (int)p.ks[2], vst = (int)p.vs[2];
 
-  // Per-head scalars (prologue).
+  // Per-head scalars, formed in the prologue once its loads are in flight.
   float bias = 0.f, eps = 0.f, tau = 0.f;
-  if (is_yat(VAR)) {
-    bias = yat_bias(p, h);
-    eps = softplus_precise(p.eps_raw[h]);
-  } else if (VAR == kStau) {
-    tau = softplus_precise(p.log_tau[h]) + 1.f;
-  }
+  auto head_scalars = [&]() {
+    if (is_yat(VAR)) {
+      bias = yat_bias(p, h);
+      eps = softplus_precise(p.eps_raw[h]);
+    } else if (VAR == kStau) {
+      tau = softplus_precise(p.log_tau[h]) + 1.f;
+    }
+  };
   const float scale = 1.0f / sqrtf((float)DK);
 
   // Query fragments: lane (half, col) holds q[my_q][16 s + 8 half + 0..7]
@@ -662,8 +672,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // tile never reads past it (entries >= T_k are masked out).
   const float* nk_slice =
       is_yat(VAR) ? p.nk + ((int64_t)b * p.Hq + h) * nk_pitch(p.Tk) : nullptr;
-  const f32x16 sinit = score_init<VAR>(bias);
-  const int b_sgpr = __builtin_amdgcn_readfirstlane(__float_as_int(bias));
+  f32x16 sinit = {};  // score_init<VAR>(bias), set in the prologue
+  int b_sgpr = 0;     // bias as a wave-uniform bit pattern, set in the prologue
 
   const int kend = p.causal ? min(p.Tk, q0 + BM) : p.Tk;
   const int n_tiles = (kend + BN - 1) / BN;
@@ -930,6 +940,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     if (t_begin + 2 < t_end) load_tile((t_begin + 2) * BN, S2{});
     if (t_begin + 3 < t_end) load_tile((t_begin + 3) * BN, S3{});
   }
+  head_scalars();
+  sinit = score_init<VAR>(bias);
+  b_sgpr = __builtin_amdgcn_readfirstlane(__float_as_int(bias));
   __builtin_amdgcn_s_waitcnt(0);
   if (is_yat(VAR)) {
     f32x16 g = sinit;
