@@ -588,13 +588,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 // It pays where the map is cheap (softmax); where the map is long (Yat,
 // s^tau) the two-stage pipeline, which starts on the first tile while the
 // next one loads, is as fast or faster, so the launcher keeps it there.
+// KH = 2: two waves per 32 query rows, one per SIMD pair slot, each taking
+// every other tile of the key range (the two tiles of an iteration are staged
+// together), and their partial O, mass and maxima merged through LDS at the
+// end.  A wave's chain of tiles -- which, with a causal mask, sets the time of
+// the longest query tiles while the CU's other work has run out -- is then
+// half as long.  One workgroup of 8 waves per CU instead of two of 4.
 constexpr int kPreTiles = 4;
 
-template <int VAR, int DK, int DV, int NW, int BN, bool PRE>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+template <int VAR, int DK, int DV, int NW, int BN, bool PRE, int KH>
+__global__ __attribute__((amdgpu_flat_work_group_size(KH * NW * 64, KH * NW * 64),
                           amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_small(Problem p) {
   constexpr int BM = NW * 32;            // query rows per workgroup
-  constexpr int NT = NW * 64;            // threads
+  constexpr int NT = NW * 64;            // threads per key half
   constexpr int KS = DK / 16;            // k-steps of the score MFMA
   constexpr int DVP = DV < 32 ? 32 : DV; // value width padded to the MFMA block
   constexpr int DB = DVP / 32;           // 32-row blocks of O^T
@@ -609,6 +615,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   static_assert(BN % 32 == 0 && BN <= 64, "tiles are 32 or 64 keys");
   constexpr int NSTG = PRE ? kPreTiles : 2;  // LDS stages
   constexpr int NSLOT = PRE ? kPreTiles : 1; // register sets of staged tiles
+  static_assert(KH == 1 || (KH == 2 && !PRE), "key halves: 1, or 2 without PRE");
 
   // Yat with d_k <= 32 forms its key norms here, from the K fragments its
   // score MFMAs read anyway: the same instruction, k-step order and start
@@ -616,15 +623,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // and wave instead of a pre-pass launch, which costs more at these widths.
   constexpr bool NK_LOCAL = yat_local_norms(VAR, DK);
 
-  // Two LDS stages (the tile being computed and the next one being filled),
-  // or one per tile with PRE.
-  __shared__ __attribute__((aligned(16))) unsigned short sK[NSTG][BN * KLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sV[NSTG][DVP * VLD];
-  __shared__ __attribute__((aligned(16))) float sNK[NSTG][BN];
-  __shared__ __attribute__((aligned(16))) float sNKw[NK_LOCAL ? NW : 1][NK_LOCAL ? BN : 4];
+  // Two LDS stages (the tiles being computed and the next ones being
+  // filled), or one per tile with PRE; each stage holds one tile per key half.
+  __shared__ __attribute__((aligned(16))) unsigned short sK[NSTG][KH][BN * KLD];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[NSTG][KH][DVP * VLD];
+  __shared__ __attribute__((aligned(16))) float sNK[NSTG][KH][BN];
+  __shared__ __attribute__((aligned(16))) float sNKw[NK_LOCAL ? KH * NW : 1][NK_LOCAL ? BN : 4];
   __shared__ float sNQ[BM];
+  // KH = 2 merge: the second half's O goes to sV, its row statistics to sK
+  static_assert(KH == 1 || (NW * 64 * DB * 16 * 4 <= (int)sizeof(sV) &&
+                            NW * 64 * 3 * 4 <= (int)sizeof(sK)), "merge buffers");
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // kh: the key half of this wave; tid, w: thread and wave within the half
+  const int kh = (int)threadIdx.x / NT;
+  const int tid = (int)threadIdx.x - kh * NT, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
 
   // Workgroup -> (query tile, batch, head).  Heads vary fastest; with a causal
@@ -732,7 +744,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       if (u < K_UNITS) {
         const int j = u / KCH, c = u % KCH;
         const int row = (j & ~31) | k_lds_row(j & 31);
-        *(u32x4*)&sK[buf][row * KLD + 8 * c] = kreg[SL][i];
+        *(u32x4*)&sK[buf][kh][row * KLD + 8 * c] = kreg[SL][i];
       }
     }
 #pragma unroll
@@ -750,12 +762,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           lo[1] = lo_halves(a2, a3);
           hi[0] = hi_halves(a0, a1);
           hi[1] = hi_halves(a2, a3);
-          *(u32x2*)&sV[buf][(8 * c + 2 * e) * VLD + 4 * g4] = lo;
-          *(u32x2*)&sV[buf][(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
+          *(u32x2*)&sV[buf][kh][(8 * c + 2 * e) * VLD + 4 * g4] = lo;
+          *(u32x2*)&sV[buf][kh][(8 * c + 2 * e + 1) * VLD + 4 * g4] = hi;
         }
       }
     }
-    if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4) *(f32x4*)&sNK[buf][4 * tid] = nkreg[SL];
+    if (is_yat(VAR) && !NK_LOCAL && tid < BN / 4) *(f32x4*)&sNK[buf][kh][4 * tid] = nkreg[SL];
   };
 
   f32x16 o[DB];
@@ -771,8 +783,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   // One tile of BN keys against the wave's 32 queries.
   auto compute = [&](auto mask_tag, int buf, int k0) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const unsigned short* K = sK[buf];
-    const unsigned short* Vt = sV[buf];
+    const unsigned short* K = sK[buf][kh];
+    const unsigned short* Vt = sV[buf][kh];
 
     // S^T = K Q^T, the KB accumulation chains interleaved.
     f32x16 sacc[KB];
@@ -809,7 +821,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         if (holds_diag(col, half))
-          sNKw[w][kb * 32 + k_lds_row(col)] = diag_of(gk[kb], col) * kNormScale;
+          sNKw[kh * NW + w][kb * 32 + k_lds_row(col)] = diag_of(gk[kb], col) * kNormScale;
     }
 
     // key k0 + 8 half + o is allowed iff o <= lim (o: the element's offset,
@@ -849,7 +861,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
           mass += e;
         }
     } else if (is_yat(VAR)) {
-      const float* NK = NK_LOCAL ? sNKw[NK_LOCAL ? w : 0] : sNK[buf];
+      const float* NK = NK_LOCAL ? sNKw[NK_LOCAL ? kh * NW + w : 0] : sNK[buf][kh];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         // (read as float vectors: this compiler mis-evaluates a bit_cast of a
@@ -934,7 +946,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld128(rq, off + 32 * s));
   }
-  if (t_begin < t_end) load_tile(t_begin * BN, S0{});
+  if (t_begin + kh < t_end) load_tile((t_begin + kh) * BN, S0{});
   if constexpr (PRE) {
     if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN, S1{});
     if (t_begin + 2 < t_end) load_tile((t_begin + 2) * BN, S2{});
@@ -944,7 +956,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   sinit = score_init<VAR>(bias);
   b_sgpr = __builtin_amdgcn_readfirstlane(__float_as_int(bias));
   __builtin_amdgcn_s_waitcnt(0);
-  if (is_yat(VAR)) {
+  if (is_yat(VAR) && kh == 0) {
     f32x16 g = sinit;
 #pragma unroll
     for (int s = 0; s < KS; ++s) g = mfma32(qf[s], qf[s], g);
@@ -955,30 +967,77 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     if (t_begin + 1 < t_end) store_tile(1, S1{});
     if (t_begin + 2 < t_end) store_tile(2, S2{});
     if (t_begin + 3 < t_end) store_tile(3, S3{});
-  } else if (t_begin < t_end) {
-    store_tile(t_begin & 1, S0{});
-    if (t_begin + 1 < t_end) load_tile((t_begin + 1) * BN, S0{});
+  } else if (t_begin + kh < t_end) {
+    store_tile(0, S0{});
+    if (t_begin + KH + kh < t_end) load_tile((t_begin + KH + kh) * BN, S0{});
   }
   __syncthreads();
   if (is_yat(VAR)) nq = sNQ[32 * w + col];
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int k0 = t * BN, buf = PRE ? t - t_begin : t & 1;
-    // every key of the tile is in this wave's future: nothing to do
-    if (!(p.causal && k0 > qw + 31)) {
+  // Iteration it covers tiles t .. t + KH - 1, this wave tile t + kh.
+  for (int t = t_begin, it = 0; t < t_end; t += KH, ++it) {
+    const int tt = t + kh, k0 = tt * BN, buf = PRE ? t - t_begin : it & 1;
+    // past the range, or every key of the tile in this wave's future: nothing to do
+    if (tt < t_end && !(p.causal && k0 > qw + 31)) {
       const bool need_mask = (p.causal && k0 + BN - 1 > qw) || (k0 + BN > p.Tk);
       if (need_mask) compute(std::true_type{}, buf, k0);
       else compute(std::false_type{}, buf, k0);
     }
     if constexpr (!PRE) {
-      if (t + 1 < t_end) {
-        // Stage t+1 was last read in iteration t-1, which every wave finished
-        // before the barrier that ended it.
+      if (tt + KH < t_end) {
+        // Stage buf ^ 1 was last read in iteration it - 1, which every wave
+        // finished before the barrier that ended it.
         store_tile(buf ^ 1, S0{});
-        if (t + 2 < t_end) load_tile(k0 + 2 * BN, S0{});
+        if (tt + 2 * KH < t_end) load_tile(k0 + 2 * KH * BN, S0{});
       }
       __syncthreads();
     }
+  }
+
+  // KH = 2: the second key half hands its partials to the first through LDS
+  // (the stages are free: the loop's last barrier, or the prologue's, has
+  // passed) and ends; the first merges them.  Yat and s^tau add O and the
+  // mass; softmax first brings both to the larger reference maximum.
+  if constexpr (KH == 2) {
+    float* mo = reinterpret_cast<float*>(&sV[0][0][0]);
+    float* ms = reinterpret_cast<float*>(&sK[0][0][0]);
+    const int slot = w * 64 + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = o[d][4 * g4 + e];
+          *(f32x4*)&mo[((d * 4 + g4) * NT + slot) * 4] = v4;
+        }
+      ms[slot] = mass;
+      ms[NT + slot] = mx;
+      ms[2 * NT + slot] = mref;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float mass1 = ms[slot], mx1 = ms[NT + slot], mref1 = ms[2 * NT + slot];
+    float f0 = 1.f, f1 = 1.f;
+    if (VAR == kSoftmax) {
+      const float m = fmaxf(mref, mref1);
+      f0 = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - m);
+      f1 = mref1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref1 - m);
+      mref = m;
+    }
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v4 = *(const f32x4*)&mo[((d * 4 + g4) * NT + slot) * 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[d][4 * g4 + e] = VAR == kSoftmax ? o[d][4 * g4 + e] * f0 + v4[e] * f1
+                                             : o[d][4 * g4 + e] + v4[e];
+      }
+    mass = VAR == kSoftmax ? mass * f0 + mass1 * f1 : mass + mass1;
+    mx = fmaxf(mx, mx1);
   }
 
   // Epilogue: combine the two lanes that share a query, normalise, store.
@@ -1048,6 +1107,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #ifndef SFS_BN
 #define SFS_BN 64
 #endif
+// The 128-row small-grid kernel splits each workgroup's key range over two
+// key halves (KH = 2) when that range spans at least this many 64-key tiles:
+// stau_gqa 76.7 -> 72.2 us; with the 4 tiles of gpt_small it is slower.
+constexpr int kKeyHalvesMinTiles = 8;
 
 // the instantiations with PRE (others compile it as false)
 template <int VAR, int DK, int DV>
@@ -1070,22 +1133,29 @@ hipError_t launch_variant(const Problem& p, hipStream_t stream) {
   const int tile_keys = p.block_rows == 128 ? 64 : 32;
   const bool pre = VAR == kSoftmax && DK <= 64 && DV <= 64 && p.kv_splits == 1 &&
                    p.Tk <= kPreTiles * tile_keys;
+  // 64-key tiles in the longest workgroup's key range (per key split)
+  const int64_t span = p.causal ? min((int64_t)p.Tk, (int64_t)nq / bh * 128) : (int64_t)p.Tk;
+  const int64_t tiles = ((span + 63) / 64 + p.kv_splits - 1) / p.kv_splits;
+  const bool key_halves = tiles >= kKeyHalvesMinTiles;
   if (p.block_rows == 256) {
     hipLaunchKernelGGL((attn_fwd_bf16<VAR, DK, DV, BN>), dim3(nq), dim3(512), 0, stream, p);
   } else if (p.block_rows == 128) {
     if (pre)
-      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, kPreBuilt<VAR, DK, DV>>),
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, kPreBuilt<VAR, DK, DV>, 1>),
                          dim3(nq, p.kv_splits), dim3(256), 0, stream, p);
+    else if (key_halves)
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, false, 2>),
+                         dim3(nq, p.kv_splits), dim3(512), 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, false>), dim3(nq, p.kv_splits),
-                         dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 4, 64, false, 1>),
+                         dim3(nq, p.kv_splits), dim3(256), 0, stream, p);
   } else {
     if (pre)
-      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32, kPreBuilt<VAR, DK, DV>>),
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32, kPreBuilt<VAR, DK, DV>, 1>),
                          dim3(nq, p.kv_splits), dim3(128), 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32, false>), dim3(nq, p.kv_splits),
-                         dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_bf16_small<VAR, DK, DV, 2, 32, false, 1>),
+                         dim3(nq, p.kv_splits), dim3(128), 0, stream, p);
   }
   return hipGetLastError();
 }

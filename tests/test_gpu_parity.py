@@ -97,6 +97,26 @@ def test_short_key_ranges_bf16(variant, shape):
     full_check(inp, variant, causal, "preload", BLOCK_ROWS)
 
 
+# 128-row workgroups whose key range spans >= 8 tiles of 64 keys take two key
+# halves: two waves per 32 query rows, alternate tiles, partials merged in LDS.
+# Causal (short and long query tiles in one launch), ragged tails, odd tile
+# counts, GQA, and d_k <= 32 (Yat norms formed in the kernel).
+KEY_HALVES = [
+    (1, 4, 2, 600, 600, 128, 128, True),
+    (2, 2, 2, 515, 515, 64, 64, True),
+    (1, 2, 1, 130, 1000, 32, 128, False),
+    (1, 2, 2, 257, 520, 16, 16, False),
+]
+
+
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("shape", KEY_HALVES, ids=lambda s: "x".join(map(str, s)))
+def test_key_halves_bf16(variant, shape):
+    B, Hq, Hkv, Tq, Tk, dk, dv, causal = shape
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=29, qk_std=1.5)
+    full_check(inp, variant, causal, "key_halves", block_rows=(128,))
+
+
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
 @pytest.mark.parametrize("shape", [(1, 2, 1, 100, 100, 32, 64, True),
                                    (2, 2, 2, 33, 90, 128, 16, False)],
@@ -255,6 +275,8 @@ def test_decode_kernel_strided_gqa_determinism(variant):
     ((1, 4, 4, 2, 2, 128, 128), (8,)),               # the decode kernel
     ((2, 6, 6, 256, 256, 32, 32), (64, 128)),        # small-grid kernels, norms formed in-kernel
     ((1, 2, 2, 100, 100, 16, 16), (64, 128)),
+    ((1, 2, 2, 600, 600, 128, 128), (128,)),        # two key halves
+    ((1, 2, 2, 600, 600, 32, 32), (128,)),          # two key halves, norms in-kernel
 ])
 def test_yat_tied_keys_with_tiny_eps(shape, rows):
     """k := q and eps = softplus(-20) ~ 2e-9: the diagonal weight is
