@@ -83,21 +83,23 @@ __device__ __forceinline__ float yat_den(float u, float nqk_scaled, float eps,
 //   Z = phi / ln 2 = max(y, c0) + log2(1 + 2^-|y|),
 // which moves the floor into the fma that forms y (2^-|y| then differs from
 // 2^-|s log2 e| by a relative 1e-6 at most).  With t = 2^-|y| in (0, 1],
-// log2(1 + t) = t P(t), P a degree-5 polynomial for log2(1 + t) / t on [0, 1]
+// log2(1 + t) = t P(t), P a degree-4 polynomial for log2(1 + t) / t on [0, 1]
 // that is minimax in relative error (Lawson's algorithm; the fit is
-// softmax_free_score_amd/stau_poly.py): relative error below 8.6e-6 with fp32
-// Horner, and t P(t) keeps that relative precision for small t, where
+// softmax_free_score_amd/stau_poly.py): relative error below 5.7e-5 with fp32
+// Horner (tau times that in the weight, well inside the 2^-9 rounding the
+// weights take for the value MFMA), and t P(t) keeps that relative precision
+// for small t, where
 // Z ~ c0 + t / ln 2.  The weight returned is Z^tau = phi^tau / (ln 2)^tau: the
 // constant factor of a head cancels in the normalised output; stau_unit gives
 // it for the mass.  Three transcendentals: exp2, log2, exp2.
 struct StauPoly {
-  float c0, c1, c2, c3, c4, c5;
+  float c0, c1, c2, c3, c4;
 };
 __device__ __forceinline__ StauPoly stau_poly() {
-  StauPoly s{1.4426828622817993f, -0.7204261422157288f, 0.4691740572452545f,
-             -0.3030361831188202f, 0.14603286981582642f, -0.03443589806556702f};
+  StauPoly s{1.4426132440567017f, -0.7169874310493469f, 0.44189882278442383f,
+             -0.22711941599845886f, 0.05965153127908707f};
   // scalar registers rather than 32-bit literals, as MapConsts above
-  asm("" : "+s"(s.c0), "+s"(s.c1), "+s"(s.c2), "+s"(s.c3), "+s"(s.c4), "+s"(s.c5));
+  asm("" : "+s"(s.c0), "+s"(s.c1), "+s"(s.c2), "+s"(s.c3), "+s"(s.c4));
   return s;
 }
 // x: the raw score q.k; mc.c_sm = log2(e) / sqrt(d_k).
@@ -105,8 +107,7 @@ __device__ __forceinline__ float stau_weight2(float x, float tau, const MapConst
                                              const StauPoly& sp) {
   const float y = fmaf(x, mc.c_sm, mc.floor2);
   const float t = __builtin_amdgcn_exp2f(-fabsf(y));
-  float l = fmaf(sp.c5, t, sp.c4);
-  l = fmaf(l, t, sp.c3);
+  float l = fmaf(sp.c4, t, sp.c3);
   l = fmaf(l, t, sp.c2);
   l = fmaf(l, t, sp.c1);
   l = fmaf(l, t, sp.c0);

@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import numpy as np
 
-DEGREE = 5
+DEGREE = 4
 
 
 def target(t: np.ndarray) -> np.ndarray:

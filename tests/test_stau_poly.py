@@ -1,10 +1,10 @@
 """The polynomial behind the s^tau tile kernels' map, on the CPU.
 
-The kernels take log2(1 + t), t = 2^-|y|, as t P(t) with P a degree-5
+The kernels take log2(1 + t), t = 2^-|y|, as t P(t) with P a degree-4
 polynomial for log2(1 + t) / t on [0, 1] (bf16_common.h, StauPoly).  These
 tests read the coefficients from that header and check them against the
 mathematics: the fit in softmax_free_score_amd/stau_poly.py reproduces them,
-their relative error in fp32 Horner evaluation is below the 8.6e-6 the header
+their relative error in fp32 Horner evaluation is below the 5.7e-5 the header
 states, and the whole base-2 map, emulated in fp32 with exactly rounded
 exp2/log2, gives phi^tau / (ln 2)^tau with phi = softplus(s) + 1e-6 ("s^tau"
 forum post, core formula) to within tau times that error."""
@@ -18,7 +18,7 @@ from conftest import ROOT
 from softmax_free_score_amd import stau_poly
 
 HEADER = os.path.join(ROOT, "softmax_free_score_amd", "csrc", "bf16_common.h")
-BOUND = 8.6e-6
+BOUND = 5.7e-5
 F32 = np.float32
 
 
@@ -63,8 +63,8 @@ def emulate_map(x, tau, c_sm, coef):
     floor2 = r32(1e-6 * np.log2(np.e))
     y = r32(x.astype(np.float64) * c_sm + floor2)
     t = r32(np.exp2(-np.abs(y.astype(np.float64))))
-    l = r32(c[5] * t + c[4])
-    for a in (c[3], c[2], c[1], c[0]):
+    l = r32(c[-1] * t + c[-2])
+    for a in c[-3::-1]:
         l = r32(l.astype(np.float64) * t + a)
     z = r32(l.astype(np.float64) * t + np.maximum(y, floor2))
     lz = r32(np.log2(z.astype(np.float64)))
