@@ -203,6 +203,19 @@ def test_kv_splits_bf16(variant, shape):
               v_rms=v_rms(inp))
 
 
+# Key splits whose chunks span >= 8 tiles take two key halves inside each chunk:
+# chunks starting at an odd tile (27 tiles in 3 chunks of 9), and causal rows
+# whose second chunk is empty for the early query tiles.
+@pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
+@pytest.mark.parametrize("case", [((1, 4, 2, 64, 1728, 128, 128, False), 3),
+                                  ((1, 2, 1, 1100, 1100, 64, 64, True), 2)],
+                         ids=lambda c: "x".join(map(str, c[0])) + f"_s{c[1]}")
+def test_kv_splits_key_halves(variant, case):
+    (B, Hq, Hkv, Tq, Tk, dk, dv, causal), splits = case
+    inp = make_custom(B, Hq, Hkv, Tq, Tk, dk, dv, "bf16", causal, seed=31, qk_std=1.5)
+    full_check(inp, variant, causal, "splits_key_halves", block_rows=(128,), kv_splits=splits)
+
+
 @pytest.mark.parametrize("variant", ["yat", "softmax", "stau"])
 @pytest.mark.parametrize("shape", [(2, 8, 2, 1, 3000, 128, 128), (4, 16, 8, 4, 2049, 64, 64),
                                    (1, 2, 1, 7, 9000, 128, 32)],
