@@ -464,7 +464,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
             xm = ok ? x : -INFINITY;
           }
           sacc[kb][r] = u;
-          mass += u;
           mx = fmaxf(mx, xm);
         }
     }
@@ -476,8 +475,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16(Problem p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
-        // Yat's mass is the sum of the bf16 weights the value MFMA takes
-        if (is_yat(VAR)) {
+        // the mass (Yat, s^tau) is the sum of the bf16 weights the value MFMA takes
+        if (is_yat(VAR) || VAR == kStau) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass, mc);
         }
@@ -902,7 +901,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KH * NW * 64, KH * NW * 64
             xm = ok ? x : -INFINITY;
           }
           sacc[kb][r] = u;
-          mass += u;
           mx = fmaxf(mx, xm);
         }
     }
@@ -916,8 +914,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KH * NW * 64, KH * NW * 64
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pw[e] = pack_bf16(sacc[kb][8 * s + 2 * e], sacc[kb][8 * s + 2 * e + 1]);
-        // Yat's mass is the sum of the bf16 weights the value MFMA takes
-        if (is_yat(VAR)) {
+        // the mass (Yat, s^tau) is the sum of the bf16 weights the value MFMA takes
+        if (is_yat(VAR) || VAR == kStau) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) mass = add_bf16_pair(pw[e], mass, mc);
         }

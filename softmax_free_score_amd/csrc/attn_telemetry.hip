@@ -18,7 +18,9 @@ namespace {
 //
 // With the forward's row normaliser (mass, and max_score for softmax) the
 // weights of every allowed pair are recomputed exactly as the forward defines
-// them (Yat: kappa rounded to bf16, as the tile kernels weight the values), and per row the pass accumulates sum w log2 w, the count of weights
+// them (Yat: kappa rounded to bf16, s^tau: phi^tau / (ln 2)^tau rounded to
+// bf16, as the tile kernels weight the values), and per row the pass
+// accumulates sum w log2 w, the count of weights
 // below the threshold and the count of allowed keys; per (head, batch, query
 // tile) it accumulates the sums that give tau* = Cov(s, ln phi(s)) /
 // Var(ln phi(s)) with s = q.k / sqrt(d_k), phi = softplus(s) + 1e-6 (the s^tau
@@ -71,6 +73,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128),
     tau = softplus_precise(p.log_tau[h]) + 1.f;
   }
   const float scale = 1.0f / sqrtf((float)DK);
+  // s^tau: the tile kernels weight the values by phi^tau / (ln 2)^tau in bf16
+  // and sum those for the mass; (ln 2)^tau brings them back to phi^tau
+  const float tau_unit = VAR == kStau ? stau_unit(tau) : 1.f;
+  constexpr float kLog2Ln2 = -0.52876637294031f;  // log2(ln 2)
 
   bf16x8 qf[KS];
   {
@@ -175,7 +181,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128, 128),
         } else if (VAR == kSoftmax) {
           wgt = __builtin_amdgcn_exp2f(fmaf(sd, scale * kLog2e, -xmax)) * inv_mass;
         } else {
-          wgt = __builtin_amdgcn_exp2f(tau * lp) * inv_mass;
+          const float zt = __builtin_amdgcn_exp2f(tau * (lp - kLog2Ln2));  // phi^tau / (ln 2)^tau
+          wgt = (float)(__bf16)zt * tau_unit * inv_mass;
         }
         wgt = ok ? wgt : 0.f;
         // w log2 w (weights below the smallest normal float add nothing)
