@@ -14,17 +14,18 @@
 //               O = sum 2^(M_s - M) O_s, l = sum 2^(M_s - M) m_s, out = O / l,
 //               mass reported relative to the row maximum x = max x_s.
 //
-// One wave per row.  The chunk statistics are read 64 at a time, one chunk
-// per lane, and reduced across the wave; the value columns (lane c holds c
-// and c + 64) then accumulate the chunks' partial O eight loads at a time, in
-// chunk order.  Every reduction has a fixed order, so the result does not
-// depend on scheduling.
+// One wave per row, chunks in batches of 32: a batch's statistics (one chunk
+// per lane) and its partial O (lane c holds value columns c and c + 64) are
+// loaded together, then the statistics are reduced across the wave and the
+// partial O accumulated in chunk order.  Every reduction has a fixed order,
+// so the result does not depend on scheduling.
 #include "attn_launch.h"
 
 namespace sfs {
 namespace {
 
 constexpr float kLn2c = 0.6931471805599453f;
+typedef float f32x4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned short to_bf16(float x) {
   return __builtin_bit_cast(unsigned short, (__bf16)x);  // round to nearest even
@@ -49,47 +50,45 @@ __global__ __launch_bounds__(256) void combine_partials(Problem p) {
   const float* po = p.part;
   const float* ps = p.part + (int64_t)S * R * dv;
 
-  float x = -INFINITY, M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int s = s0 + lane;
-    if (s < S) {
-      const float* st = ps + ((int64_t)s * R + r) * 4;
-      x = fmaxf(x, st[1]);
-      M = fmaxf(M, st[2]);
-    }
-  }
-  x = wave_max(x);
-  M = wave_max(M);
-  float mass = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    // lane l: the weight and weighted mass of chunk s0 + l
-    float wgt = 0.f, m = 0.f;
-    const int s = s0 + lane;
-    if (s < S) {
-      const float* st = ps + ((int64_t)s * R + r) * 4;
-      wgt = 1.f;
-      if (p.variant == kSoftmax) wgt = st[2] == -INFINITY ? 0.f : exp2f(st[2] - M);
-      m = wgt * st[0];
-    }
-    mass += wave_sum(m);
-    const int nb = min(64, S - s0);
-    for (int t = 0; t < nb; t += 8) {
-      float a0[8], a1[8];
+  // Chunks in batches of kBatch: every load of a batch -- the statistics of
+  // chunk s0 + lane and the partial O of each chunk of the batch -- is issued
+  // before any is used, so a batch costs one memory round trip.
+  constexpr int kBatch = 32;
+  float x = -INFINITY, M = -INFINITY, mass = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    const int nb = min(kBatch, S - s0);
+    f32x4s st = {0.f, -INFINITY, -INFINITY, 0.f};
+    if (lane < nb) st = *(const f32x4s*)(ps + ((int64_t)(s0 + lane) * R + r) * 4);
+    float a0[kBatch], a1[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a0[u] = a1[u] = 0.f;
-        if (t + u < nb) {
-          const float* row = po + ((int64_t)(s0 + t + u) * R + r) * dv;
-          if (lane < dv) a0[u] = row[lane];
-          if (lane + 64 < dv) a1[u] = row[lane + 64];
-        }
+    for (int u = 0; u < kBatch; ++u) {
+      a0[u] = a1[u] = 0.f;
+      if (u < nb) {
+        const float* row = po + ((int64_t)(s0 + u) * R + r) * dv;
+        if (lane < dv) a0[u] = row[lane];
+        if (lane + 64 < dv) a1[u] = row[lane + 64];
       }
+    }
+    // batch maxima; softmax rescales what the earlier batches summed
+    const float xb = wave_max(st[1]), Mb = wave_max(st[2]);
+    x = fmaxf(x, xb);
+    float fo = 1.f;  // factor for the sums so far (softmax)
+    if (p.variant == kSoftmax) {
+      const float Mn = fmaxf(M, Mb);
+      fo = M == -INFINITY ? 0.f : exp2f(M - Mn);
+      M = Mn;
+    }
+    // lane l: the weight of chunk s0 + l
+    float wgt = lane < nb ? 1.f : 0.f;
+    if (p.variant == kSoftmax && lane < nb) wgt = st[2] == -INFINITY ? 0.f : exp2f(st[2] - M);
+    mass = mass * fo + wave_sum(wgt * st[0]);
+    o0 *= fo;
+    o1 *= fo;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wu = __shfl(wgt, t + u, 64);  // 0 past the last chunk
-        o0 = fmaf(wu, a0[u], o0);
-        o1 = fmaf(wu, a1[u], o1);
-      }
+    for (int u = 0; u < kBatch; ++u) {
+      const float wu = __shfl(wgt, u, 64);  // 0 past the last chunk
+      o0 = fmaf(wu, a0[u], o0);
+      o1 = fmaf(wu, a1[u], o1);
     }
   }
   float inv;
