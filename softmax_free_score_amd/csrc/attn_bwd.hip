@@ -983,14 +983,17 @@ __global__ __launch_bounds__(256) void norms_plus_bias_bf16(const unsigned short
   const uint32_t bytes = slice_bytes(T, s2, DK);
   const rsrc_t r = make_rsrc(base, bytes);
   const uint32_t off = row < T ? (uint32_t)(((int64_t)row * s2 + 8 * half) * 2) : bytes;
+  // the row's loads first: b's parameter load and softplus run under them
+  u32x4 xr[DK / 16];
+#pragma unroll
+  for (int s = 0; s < DK / 16; ++s) xr[s] = ld128(r, off + 32 * s);
   const float bias = softplus_precise(b_raw[h]);  // as head_consts forms it
   f32x16 g;
 #pragma unroll
   for (int i = 0; i < 16; ++i) g[i] = bias;
 #pragma unroll
   for (int s = 0; s < DK / 16; ++s)
-    g = mfma32(__builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)),
-               __builtin_bit_cast(bf16x8, ld128(r, off + 32 * s)), g);
+    g = mfma32(__builtin_bit_cast(bf16x8, xr[s]), __builtin_bit_cast(bf16x8, xr[s]), g);
   if (row < T && holds_diag(col, half))
     out[((int64_t)b * Hq + h) * nk_pitch(T) + row] = diag_of(g, col) * kNormScale;
 }
