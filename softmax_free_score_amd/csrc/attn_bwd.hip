@@ -38,7 +38,7 @@
 //     so the accumulator of lane (half, col) holds key col and queries
 //     16 (r / 8) + 8 half + r % 8 in natural order: packed to bf16 it is the B
 //     operand of dV^T += dO^T P and dK^T += Q^T G, whose A operands (dO^T,
-//     Q^T, queries contiguous) are written transposed into LDS on the way in.
+//     Q^T) come from the same row-major tiles by transposing LDS reads.
 //   * attn_bwd_q is the mirror image: S^T = K Q^T and dP^T = V dO^T with the
 //     lane's query fragments in registers, then dQ^T += K^T G^T with K^T in
 //     LDS.
@@ -80,21 +80,28 @@ __device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x 
 // ds_read_b64_tr_b16 per lane: within each group of 16 lanes, source lane c
 // addresses tile row base + c / 4, columns cb + 4 (c % 4) .. + 3, and the
 // hardware returns to lane i of the group column cb + i of rows base .. base
-// + 3 (lane mapping measured on gfx950).  Columns at or past `width` (a tile
-// narrower than 32) wrap to width - 16 .. width - 1; those rows of the
-// product are not used.
+// + 3 (lane mapping measured on gfx950).
+//
+// The lane's part of the address is formed once by tr_lane_off (elements);
+// tr_frag_at(R + off, ld, c0, s) then reads at (16 s + 8 j) ld + c0, j = 0, 1,
+// offsets the reads carry as immediates.  (k_lds_row swaps row bits 2 and 3,
+// so tile row 16 s + 8 (g >> 1) + 4 j + (c >> 2), g = lane / 16, sits at
+// 16 s + 8 j + 4 (g >> 1) + (c >> 2).)  Needs c0 + 32 <= width, or c0 = 0 for
+// a tile narrower than 32, whose columns at or past `width` wrap to
+// width - 16 .. width - 1: those rows of the product are not used.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned short* R, int ld, int c0, int s,
-                                          int lane, int width) {
+__device__ __forceinline__ int tr_lane_off(int lane, int ld, int width) {
   const int g = lane >> 4, c = lane & 15;
-  int cb = c0 + 16 * (g & 1) + 4 * (c & 3);
+  int cb = 16 * (g & 1) + 4 * (c & 3);
   if (cb >= width) cb -= 16;
+  return (4 * (g >> 1) + (c >> 2)) * ld + cb;
+}
+__device__ __forceinline__ bf16x8 tr_frag_at(const unsigned short* R, int ld, int c0, int s) {
   u32x4 out;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int row = 16 * s + 8 * (g >> 1) + 4 * j + (c >> 2);
     const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(R + k_lds_row(row) * ld + cb));
+        (__attribute__((address_space(3))) i16x4*)(R + (16 * s + 8 * j) * ld + c0));
     const u32x2 xx = __builtin_bit_cast(u32x2, x);
     out[2 * j] = xx[0];
     out[2 * j + 1] = xx[1];
@@ -252,15 +259,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   constexpr int KS = DK / 16, VS = DV / 16, FS = KS > VS ? KS : VS;
   constexpr int DKP = DK < 32 ? 32 : DK, DVP = DV < 32 ? 32 : DV;
   constexpr int KB = DKP / 32, VB = DVP / 32, AB = KB > VB ? KB : VB;
-  constexpr int QLD = DK + 8, OLD = DV + 8, TLD = BQ + 8;
+  constexpr int QLD = DK + 8, OLD = DV + 8;
   constexpr int Q_UNITS = (BQ / 4) * (DK / 8), O_UNITS = (BQ / 4) * (DV / 8);
   constexpr int UNITS = Q_UNITS + O_UNITS;
   constexpr int PER_T = (UNITS + NT - 1) / NT;
 
   __shared__ __attribute__((aligned(16))) unsigned short sQ[NS][BQ * QLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sQt[NS][DKP * TLD];
   __shared__ __attribute__((aligned(16))) unsigned short sO[NS][BQ * OLD];
-  __shared__ __attribute__((aligned(16))) unsigned short sOt[NS][DVP * TLD];
   __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
   __shared__ __attribute__((aligned(16))) float sZ[NS][BQ];
   __shared__ __attribute__((aligned(16))) float sNQ[NS][BQ];
@@ -269,6 +274,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const bool is_a = w < NP;
+  const int trq = tr_lane_off(lane, QLD, DK), tro = tr_lane_off(lane, OLD, DV);
   const int pr = w & (NP - 1);
   // Workgroup -> (key tile, batch, kv head), heads fastest.  With a causal
   // mask the first key tiles have the most queries and go first.  (Grouping
@@ -363,33 +369,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
       if (is_yat(VAR)) st_nq = p.nq[idx];
     }
   };
-  // 4 rows x 8 columns -> 4 rows of the row-major tile (rows permuted) and
-  // 8 rows of 4 of the transposed one.
-  auto put = [&](const u32x4* rows, int g4, int c, unsigned short* R, int ld,
-                 unsigned short* Tr) {
+  // 4 rows x 8 columns -> 4 rows of the row-major tile (rows permuted)
+  auto put = [&](const u32x4* rows, int g4, int c, unsigned short* R, int ld) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) *(u32x4*)&R[k_lds_row(4 * g4 + r) * ld + 8 * c] = rows[r];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const unsigned a0 = rows[0][e], a1 = rows[1][e], a2 = rows[2][e], a3 = rows[3][e];
-      u32x2 lo, hi;
-      lo[0] = lo_halves(a0, a1);
-      lo[1] = lo_halves(a2, a3);
-      hi[0] = hi_halves(a0, a1);
-      hi[1] = hi_halves(a2, a3);
-      *(u32x2*)&Tr[(8 * c + 2 * e) * TLD + 4 * g4] = lo;
-      *(u32x2*)&Tr[(8 * c + 2 * e + 1) * TLD + 4 * g4] = hi;
-    }
   };
   auto store = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int u = tid + i * NT;
       if (u < Q_UNITS) {
-        put(st[i], u % (BQ / 4), u / (BQ / 4), sQ[slot], QLD, sQt[slot]);
+        put(st[i], u % (BQ / 4), u / (BQ / 4), sQ[slot], QLD);
       } else if (u < UNITS) {
         const int u2 = u - Q_UNITS;
-        put(st[i], u2 % (BQ / 4), u2 / (BQ / 4), sO[slot], OLD, sOt[slot]);
+        put(st[i], u2 % (BQ / 4), u2 / (BQ / 4), sO[slot], OLD);
       }
     }
     if (tid < BQ) {
@@ -471,8 +464,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
       const bf16x8 bop = __builtin_bit_cast(bf16x8, pk[s]);
 #pragma unroll
       for (int i = 0; i < VB; ++i)
-        acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sOt[slot][(32 * i + col) * TLD + 16 * s + 8 * half]),
-                        bop, acc[i]);
+        acc[i] = mfma32(tr_frag_at(sO[slot] + tro, OLD, 32 * i, s), bop, acc[i]);
     }
   };
   // B: dP of the tile in `slot`, A's factors from sS[ss], the gradient scores
@@ -522,8 +514,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
       const bf16x8 bop = __builtin_bit_cast(bf16x8, pk[s]);
 #pragma unroll
       for (int i = 0; i < KB; ++i)
-        acc[i] = mfma32(__builtin_bit_cast(bf16x8, *(const u32x4*)&sQt[slot][(32 * i + col) * TLD + 16 * s + 8 * half]),
-                        bop, acc[i]);
+        acc[i] = mfma32(tr_frag_at(sQ[slot] + trq, QLD, 32 * i, s), bop, acc[i]);
     }
   };
   // A: S, weights and factors of the tile at `x` in `slot`
@@ -562,6 +553,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
     map_tile(cur, 0, 0, pk_cur);
   }
   __syncthreads();
+  // Every load issued so far has landed (vmcnt 0).  Without this wait the
+  // compiler cannot tell at the loop head that the fragments in `frag` are
+  // complete (on the path with no tiles the prologue waits for nothing), and
+  // makes each score or dP MFMA of the loop wait for all loads in flight,
+  // including the staging loads issued earlier in the same iteration.
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 
   for (int it = 0; it < n_it; ++it) {
     const int slot = it % NS;
@@ -579,6 +576,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
           hc = head_consts<VAR, DK>(p, hk * g + nxt.gi);
           hc_gi = nxt.gi;
           load_nk(nxt.gi);
+          // as before the loop: |k|^2 + b lands here, so that the maps of
+          // the other iterations do not wait for the staging loads
+          if (is_yat(VAR)) __builtin_amdgcn_s_waitcnt(0x0f70);
         }
         u32x4 pk_nxt[2];
         map_tile(nxt, (it + 1) % NS, (it + 1) & 1, pk_nxt);
@@ -678,6 +678,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
+  const int trk = tr_lane_off(lane, KLD, DK);
   const int n_qt = (p.Tq + BM - 1) / BM;
   const int nbh = p.B * p.Hq;
   int qt = blockIdx.x / nbh;
@@ -858,7 +859,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
       const bf16x8 bg = __builtin_bit_cast(bf16x8, pg[s]);
 #pragma unroll
       for (int i = 0; i < KB; ++i)
-        accQ[i] = mfma32(tr_frag(sK[buf], KLD, 32 * i, s, lane, DK), bg, accQ[i]);
+        accQ[i] = mfma32(tr_frag_at(sK[buf] + trk, KLD, 32 * i, s), bg, accQ[i]);
     }
   };
 
